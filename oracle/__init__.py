@@ -1,0 +1,30 @@
+"""CPU oracle for the batch-invariant fused linear log-probability forward.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute anything in this package: only the test suite, the smoke check in
+``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` use it.
+
+The oracle is written from the RL-Kernel pull-request page
+"feat(linear-logp): add batch-invariant fused SM90 operator" (PR #337) and
+shares no code, constant table or helper with the HIP library.  Every value is
+computed in IEEE binary64 from the exact values of the bf16 / fp32 inputs.
+
+Modules
+-------
+linear_logp
+    ``decode_bf16``               exact bf16 -> float64 decode from the bit pattern
+    ``linear_logp``               the plain definition (dgemm + explicit max / exp / log)
+    ``vocab_splits``              the V-only contiguous split policy
+    ``split_merge_linear_logp``   the method's own steps: per-split online
+                                  (max, sum-exp) partials, then the ascending combine
+    ``brute_force_linear_logp``   pure-Python ``math.fsum`` version for tiny inputs
+"""
+
+from .linear_logp import (  # noqa: F401
+    decode_bf16,
+    to_f64,
+    linear_logp,
+    vocab_splits,
+    split_merge_linear_logp,
+    brute_force_linear_logp,
+)
