@@ -1,0 +1,173 @@
+#!/usr/bin/env python3
+"""Throughput of the batch-invariant fused linear log-probability forward on
+one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline]
+                    [--no-cpu-baseline]
+
+One step is one full pass of the hot path over one batch: bilogp_partials
+(fused bf16-MFMA projection + per-split online softmax) followed by
+bilogp_merge (ascending split merge), i.e. exactly bilogp_forward_ex with a
+caller workspace.  Inputs are synthetic, seeded, and resident in HBM before
+timing starts.  W untimed warmup steps, then K timed steps between device
+synchronisations.  HIP events recorded on the launch stream bracket each
+kernel so the projection kernel's own average duration is measured live.
+
+Prints ONE JSON line with the throughput (tokens/s), the roofline of the
+projection kernel (bf16 MFMA bound) and the fp64 CPU oracle timed on a
+bounded row sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/s + TFLOP/s (MFMA %peak), linear-logp N=4096 H=4096 V=128256 bf16"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="headline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="rows of the workload the CPU oracle is timed on")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(N, H, V, S, bias_bytes):
+    """Bytes the forward must move at least once: W, hidden, targets, bias,
+    the partials written and read back, target logits, and the outputs."""
+    return (V * H * 2 + N * H * 2 + N * 8 + bias_bytes + 2 * N * S * 8 + 2 * N * 4 + 2 * N * 4)
+
+
+def cpu_baseline(inp, rows_n, seed=7):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("internal_api") in ("openblas", "mkl", "blis")] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    h = inp["hidden"].reshape(-1, inp["hidden"].shape[-1]).cpu()
+    t = inp["target"].reshape(-1).cpu()
+    w = inp["weight"].cpu()
+    b = None if inp["bias"] is None else inp["bias"].cpu()
+    N = h.shape[0]
+    g = np.random.default_rng(seed)
+    rows = np.sort(g.choice(N, size=min(rows_n, N), replace=False))
+    t0 = time.perf_counter()
+    oracle.linear_logp(h, w, t, b, rows=rows)
+    dt = time.perf_counter() - t0
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(rows)} seeded rows of the {N}-row workload (fp64 numpy/BLAS, "
+                      f"bf16 decode included), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); rows are independent, "
+              "so N GPUs would each run this same single-GPU step on their own rows.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import invariant_linear_log_amd as ila
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = synth.make_inputs(args.workload, device=dev)
+    wl = inp["workload"]
+    h = inp["hidden"].reshape(-1, wl.H).contiguous()
+    t = inp["target"].reshape(-1).contiguous()
+    w = inp["weight"]
+    b = inp["bias"]
+    N, H, V = wl.N, wl.H, wl.V
+    S = ila.bilogp_num_vocab_splits(V)
+    logp = torch.empty(N, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    ws = ila.workspace_for(N, V, dev)
+    stream = torch.cuda.Stream(device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev0=None, ev1=None, ev2=None):
+        if ev0 is not None:
+            ev0.record(stream)
+        ila.bilogp_partials(h, w, t, b, ws, stream=stream)
+        if ev1 is not None:
+            ev1.record(stream)
+        ila.bilogp_merge(t, ws, logp, lse, V, stream=stream)
+        if ev2 is not None:
+            ev2.record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(*evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    proj_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    merge_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    avg_proj_s = sum(proj_ms) / K / 1e3
+    avg_merge_s = sum(merge_ms) / K / 1e3
+    flops = 2.0 * N * H * V
+    tflops_proj = flops / avg_proj_s / 1e12
+    ms_per_step = elapsed / K * 1e3
+    tokens_per_s = N * K / elapsed
+    tflops_step = flops / (elapsed / K) / 1e12
+    ok = bool(torch.all(torch.isfinite(lse))) and bool(torch.all(logp <= 0))
+    bias_bytes = 0 if b is None else V * b.element_size()
+
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "N": N, "H": H, "V": V,
+                   "lead_shape": list(wl.lead_shape),
+                   "bias": wl.bias, "splits": S, "tokens_per_step": N},
+        "tflops": tflops_step,
+        "mfma_peak_frac": tflops_step / PEAK_BF16_TFLOPS,
+        "kernel_ms": {"proj_lse": avg_proj_s * 1e3, "merge": avg_merge_s * 1e3},
+        "outputs_sane": ok,
+        "roofline": {"bound": "mfma", "kernel": "proj_lse_kernel",
+                     "achieved": tflops_proj, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops_proj / PEAK_BF16_TFLOPS,
+                     "algorithmic_flops": flops,
+                     "algorithmic_bytes": algorithmic_bytes(N, H, V, S, bias_bytes),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,153 @@
+/*
+ * bilogp.h - batch-invariant fused linear log-probability forward for AMD
+ * Instinct MI355X (gfx950).  Plain C ABI: device pointers, sizes, a stream.
+ *
+ * The operation (RL-Kernel PR #337, "feat(linear-logp): add batch-invariant
+ * fused SM90 operator": walkthrough, sequence diagram and description):
+ *
+ *     z[i, v]  = sum_k hidden[i, k] * W[v, k]  (+ bias[v])     v in [0, V)
+ *     lse[i]   = log( sum_v exp(z[i, v]) )
+ *     logp[i]  = z[i, target[i]] - lse[i]
+ *
+ * The [N, V] logits are never stored.  The vocabulary is cut into tiles of
+ * bilogp_vtile_cols() columns and the tiles into at most bilogp_max_splits()
+ * contiguous splits whose count depends on V only (the page's annotation on
+ * select_batch_invariant_vocab_splits).  Each split yields a per-row partial
+ * online-softmax state (running max, rescaled sum of exponentials); the
+ * partials are combined in ascending split order ("What this PR changes").
+ * The bits of row i's outputs depend only on row i's inputs, W, bias, H and
+ * V: never on N, on the position of the row in the batch, on the other rows,
+ * or on the number of compute units.
+ *
+ * Forward only.  The page's first contract excludes the backward; the entry
+ * points take no gradient state.
+ *
+ * Conventions for every entry point
+ *  - Ownership: the caller owns every buffer.  The library keeps no device
+ *    state between calls; bilogp_forward allocates and frees its workspace
+ *    stream-ordered on `stream`.
+ *  - Asynchrony: all device work is enqueued on `stream` (a hipStream_t;
+ *    NULL = the null stream).  No entry point synchronizes; inputs must stay
+ *    alive until the stream reaches the work.
+ *  - Errors: no entry point throws.  On any error nothing is launched and the
+ *    outputs are left untouched; a status is returned and a thread-local
+ *    message is available from bilogp_last_error().
+ *  - Failing closed (the page's registry maps unsupported platforms to an
+ *    explicit error rather than a generic fallback): a device that is not
+ *    gfx950 gives BILOGP_E_UNSUPPORTED; there is no other code path.
+ *  - Thread safety: entry points are reentrant.  Concurrent calls on
+ *    different streams must use different workspaces.
+ */
+#ifndef BILOGP_H
+#define BILOGP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BILOGP_ABI_VERSION 1
+
+typedef enum bilogp_status {
+  BILOGP_OK = 0,
+  BILOGP_E_INVALID_ARG = 1,   /* null pointer, bad size, aliasing outputs, bad enum */
+  BILOGP_E_UNSUPPORTED = 2,   /* not gfx950, pointer not on the current device,
+                                 H % 8 != 0, misaligned input */
+  BILOGP_E_WORKSPACE = 3,     /* workspace missing or smaller than bilogp_workspace_bytes */
+  BILOGP_E_HIP = 4            /* a HIP runtime call or launch failed */
+} bilogp_status;
+
+typedef enum bilogp_bias_dtype {
+  BILOGP_BIAS_NONE = 0,
+  BILOGP_BIAS_BF16 = 1,
+  BILOGP_BIAS_F32 = 2
+} bilogp_bias_dtype;
+
+/* BILOGP_ABI_VERSION of the built library. */
+int bilogp_abi_version(void);
+
+/* Width of a vocabulary tile in columns.  Part of the bit contract. */
+int bilogp_vtile_cols(void);
+
+/* Largest number of vocabulary splits.  Part of the bit contract. */
+int bilogp_max_splits(void);
+
+/* Vocabulary tiles per split for vocabulary size V: with T = ceil(V / tile
+ * width), ceil(T / bilogp_max_splits()).  The page gives the policy's
+ * constraints (annotation on select_batch_invariant_vocab_splits: at most
+ * the maximum number of non-empty contiguous ranges, chosen from V only) but
+ * its formula is cut off; this is the plainest reading.  Split k covers
+ * tiles [k * per_split, min((k + 1) * per_split, T)).  Returns 0 if V <= 0
+ * or V > 2^30.  Takes no N and no device property, by construction. */
+int bilogp_vtiles_per_split(int64_t V);
+
+/* Number of splits S = ceil(T / per_split) for vocabulary size V (0 if V is
+ * out of range). */
+int bilogp_num_vocab_splits(int64_t V);
+
+/* Bytes of device workspace bilogp_forward_ex needs for N rows and vocabulary
+ * size V: the [N, S] partial (max, sum-exp) pairs and the [N] target logits,
+ * each 256-byte aligned.  0 for N == 0; (size_t)-1 for invalid N or V. */
+size_t bilogp_workspace_bytes(int64_t N, int64_t V);
+
+/* Fused forward with an optional fp32 bias and a library-managed workspace
+ * (stream-ordered hipMallocAsync / hipFreeAsync on `stream`).
+ *
+ *   hidden   device, bf16 [N, H] row-major (K contiguous), 16-byte aligned
+ *   weight   device, bf16 [V, H] row-major (K contiguous), 16-byte aligned
+ *   target   device, int64 [N]; a value outside [0, V) yields logp = NaN for
+ *            that row (lse stays valid) - a range check needs a host sync,
+ *            which this entry point never does
+ *   bias     device, fp32 [V], or NULL for no bias
+ *   logp_out device, fp32 [N]   (written)
+ *   lse_out  device, fp32 [N]   (written)
+ *   0 <= N <= 2^32 (N == 0 is a successful no-op), 8 <= H <= 2^20 with
+ *   H % 8 == 0, 1 <= V <= 2^30.  The outputs must not overlap each other, an
+ *   input or the workspace.
+ */
+bilogp_status bilogp_forward(const void* hidden, const void* weight, const int64_t* target,
+                             const float* bias, float* logp_out, float* lse_out,
+                             int64_t N, int64_t H, int64_t V, void* stream);
+
+/* As bilogp_forward, with the bias dtype given explicitly (bias may be bf16
+ * or fp32, [V]; NULL iff bias_dtype == BILOGP_BIAS_NONE) and a caller-owned
+ * device workspace of at least bilogp_workspace_bytes(N, V) bytes, 256-byte
+ * aligned.  Allocates nothing. */
+bilogp_status bilogp_forward_ex(const void* hidden, const void* weight, const int64_t* target,
+                                const void* bias, int bias_dtype, float* logp_out,
+                                float* lse_out, int64_t N, int64_t H, int64_t V,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two halves of bilogp_forward_ex, for callers that schedule them
+ * separately (a timing harness, or a vocabulary-sharded caller that exchanges
+ * partials between the halves).  Same arguments and checks as
+ * bilogp_forward_ex; the workspace carries the state between the calls.
+ *
+ * bilogp_partials: the fused projection and per-split online softmax; writes
+ * the workspace's [N, S] (max, sum-exp) partials and the [N] target logits
+ * (RL-Kernel PR #337, description: split-V from V only, partial online-
+ * softmax states per contiguous split).
+ */
+bilogp_status bilogp_partials(const void* hidden, const void* weight, const int64_t* target,
+                              const void* bias, int bias_dtype, int64_t N, int64_t H, int64_t V,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* bilogp_merge: the ascending combine of the partials left in `workspace` by
+ * bilogp_partials for the same N, V and target (PR #337, description:
+ * "ascending combine"); writes logp_out and lse_out, fp32 [N]. */
+bilogp_status bilogp_merge(const int64_t* target, const void* workspace, size_t workspace_bytes,
+                           float* logp_out, float* lse_out, int64_t N, int64_t V, void* stream);
+
+/* Static description of a status code. */
+const char* bilogp_status_string(int status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* bilogp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BILOGP_H */

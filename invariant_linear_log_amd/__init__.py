@@ -1,0 +1,117 @@
+"""Batch-invariant fused linear log-probability forward for AMD MI355X (gfx950).
+
+    logp, lse = invariant_linear_log_amd.forward(hidden, weight, target, bias=None)
+
+computes, per row of ``hidden[..., H]`` (bf16), the logits ``hidden . W^T
+(+ bias)`` over the vocabulary ``W[V, H]`` (bf16) without storing them, and
+returns the log-probability of ``target`` and the log-sum-exp of the logits
+(fp32, shaped like ``target``).  Output bits never depend on the number of
+rows, their order or neighbours, the stream, or the GPU's compute-unit
+count.  Forward only: inputs that require grad while autograd is enabled are
+rejected (RL-Kernel PR #337, author's annotation on the ``requires_grad``
+check: the backward is outside the first contract, so the path fails closed).
+
+The C entry points of ``include/bilogp.h`` are available under the same
+names (``bilogp_forward``, ``bilogp_forward_ex``, ``bilogp_workspace_bytes``,
+...), marshalling torch tensors to device pointers and the current stream.
+"""
+
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from ._binding import (  # noqa: F401
+    BILOGP_BIAS_BF16,
+    BILOGP_BIAS_F32,
+    BILOGP_BIAS_NONE,
+    BILOGP_E_HIP,
+    BILOGP_E_INVALID_ARG,
+    BILOGP_E_UNSUPPORTED,
+    BILOGP_E_WORKSPACE,
+    BILOGP_OK,
+    BilogpError,
+    LIB_PATH,
+    bilogp_abi_version,
+    bilogp_forward,
+    bilogp_forward_ex,
+    bilogp_last_error,
+    bilogp_max_splits,
+    bilogp_merge,
+    bilogp_num_vocab_splits,
+    bilogp_partials,
+    bilogp_status_string,
+    bilogp_vtile_cols,
+    bilogp_vtiles_per_split,
+    bilogp_workspace_bytes,
+    load_library,
+)
+
+__all__ = ["forward", "workspace_for", "BilogpError", "load_library"]
+
+
+def workspace_for(N: int, V: int, device) -> Optional[torch.Tensor]:
+    """A uint8 device tensor big enough for ``bilogp_forward_ex`` (None if N == 0)."""
+    nbytes = bilogp_workspace_bytes(N, V)
+    if nbytes == (1 << 64) - 1:
+        raise ValueError(f"invalid sizes N={N}, V={V}")
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def forward(hidden: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
+            bias: Optional[torch.Tensor] = None, *, check_targets: bool = True,
+            workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(logp, lse), each fp32 with ``target``'s shape.
+
+    hidden  [..., H] bf16        weight [V, H] bf16
+    target  [...] int64 (the leading shape of hidden); a zero-stride
+            (expanded) target is accepted and made contiguous
+    bias    [V] bf16 or fp32, optional
+
+    ``check_targets`` verifies 0 <= target < V on the host first (one device
+    sync); without it an out-of-range target gives NaN for that row.
+    """
+    if torch.is_grad_enabled() and (hidden.requires_grad or weight.requires_grad or
+                                    (bias is not None and bias.requires_grad)):
+        raise RuntimeError("batch-invariant linear logp is forward-only: call it under "
+                           "torch.no_grad() or with inputs that do not require grad")
+    if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise TypeError("hidden and weight must be bfloat16")
+    if target.dtype != torch.int64:
+        raise TypeError("target must be int64")
+    if weight.dim() != 2 or hidden.dim() < 1 or hidden.shape[-1] != weight.shape[1]:
+        raise ValueError(f"shape mismatch: hidden {tuple(hidden.shape)}, "
+                         f"weight {tuple(weight.shape)}")
+    lead_shape = hidden.shape[:-1]
+    if tuple(target.shape) != tuple(lead_shape):
+        raise ValueError(f"target shape {tuple(target.shape)} != {tuple(lead_shape)}")
+    V, H = weight.shape
+    if bias is not None:
+        if bias.dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError("bias must be bfloat16 or float32")
+        if tuple(bias.shape) != (V,):
+            raise ValueError(f"bias shape {tuple(bias.shape)} != ({V},)")
+    tensors = [hidden, weight, target] + ([bias] if bias is not None else [])
+    dev = hidden.device
+    if dev.type != "cuda" or any(t.device != dev for t in tensors):
+        raise ValueError("all tensors must be on the same GPU")
+
+    with torch.no_grad():
+        hidden_2d = hidden.reshape(-1, H).contiguous()
+        weight_2d = weight.contiguous()
+        target_1d = target.reshape(-1).contiguous()
+        bias_1d = None if bias is None else bias.contiguous()
+        N = hidden_2d.shape[0]
+        if check_targets and N > 0:
+            lo, hi = int(target_1d.min()), int(target_1d.max())
+            if lo < 0 or hi >= V:
+                raise ValueError(f"target outside [0, {V}): min {lo}, max {hi}")
+        logp = torch.empty(N, dtype=torch.float32, device=dev)
+        lse = torch.empty(N, dtype=torch.float32, device=dev)
+        if N > 0:
+            ws = workspace if workspace is not None else workspace_for(N, V, dev)
+            bilogp_forward_ex(hidden_2d, weight_2d, target_1d, bias_1d, logp, lse, ws)
+    return logp.reshape(lead_shape), lse.reshape(lead_shape)

@@ -1,0 +1,204 @@
+"""ctypes binding of ``libbilogp.so`` (declared in ``include/bilogp.h``).
+
+Argument marshalling only: every step of the forward runs in the library's
+HIP kernels.  PyTorch supplies device memory and the current stream.  If the
+library is missing or cannot be loaded, every call raises; there is no other
+code path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbilogp.so")
+
+BILOGP_OK = 0
+BILOGP_E_INVALID_ARG = 1
+BILOGP_E_UNSUPPORTED = 2
+BILOGP_E_WORKSPACE = 3
+BILOGP_E_HIP = 4
+
+BILOGP_BIAS_NONE = 0
+BILOGP_BIAS_BF16 = 1
+BILOGP_BIAS_F32 = 2
+
+_STATUS_NAMES = {0: "BILOGP_OK", 1: "BILOGP_E_INVALID_ARG", 2: "BILOGP_E_UNSUPPORTED",
+                 3: "BILOGP_E_WORKSPACE", 4: "BILOGP_E_HIP"}
+
+# name -> (restype, argtypes); mirrors include/bilogp.h
+_VP = ctypes.c_void_p
+_I64 = ctypes.c_int64
+SIGNATURES = {
+    "bilogp_abi_version": (ctypes.c_int, []),
+    "bilogp_vtile_cols": (ctypes.c_int, []),
+    "bilogp_max_splits": (ctypes.c_int, []),
+    "bilogp_vtiles_per_split": (ctypes.c_int, [_I64]),
+    "bilogp_num_vocab_splits": (ctypes.c_int, [_I64]),
+    "bilogp_workspace_bytes": (ctypes.c_size_t, [_I64, _I64]),
+    "bilogp_forward": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _VP]),
+    "bilogp_forward_ex": (ctypes.c_int, [_VP, _VP, _VP, _VP, ctypes.c_int, _VP, _VP, _I64, _I64,
+                                         _I64, _VP, ctypes.c_size_t, _VP]),
+    "bilogp_partials": (ctypes.c_int, [_VP, _VP, _VP, _VP, ctypes.c_int, _I64, _I64, _I64, _VP,
+                                       ctypes.c_size_t, _VP]),
+    "bilogp_merge": (ctypes.c_int, [_VP, _VP, ctypes.c_size_t, _VP, _VP, _I64, _I64, _VP]),
+    "bilogp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "bilogp_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+_lock = threading.Lock()
+
+
+class BilogpError(RuntimeError):
+    """A non-OK status from the library."""
+
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.detail = detail
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {detail}")
+
+
+def load_library(path: str = LIB_PATH):
+    """Load (once) and return the ctypes handle of the HIP library."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it with `python -m invariant_linear_log_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+        return lib
+
+
+def _check(status: int) -> None:
+    if status != BILOGP_OK:
+        lib = load_library()
+        raise BilogpError(status, lib.bilogp_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ---------------------------------------------------------------- plain queries
+def bilogp_abi_version() -> int:
+    return load_library().bilogp_abi_version()
+
+
+def bilogp_vtile_cols() -> int:
+    return load_library().bilogp_vtile_cols()
+
+
+def bilogp_max_splits() -> int:
+    return load_library().bilogp_max_splits()
+
+
+def bilogp_vtiles_per_split(V: int) -> int:
+    return load_library().bilogp_vtiles_per_split(V)
+
+
+def bilogp_num_vocab_splits(V: int) -> int:
+    return load_library().bilogp_num_vocab_splits(V)
+
+
+def bilogp_workspace_bytes(N: int, V: int) -> int:
+    return load_library().bilogp_workspace_bytes(N, V)
+
+
+def bilogp_status_string(status: int) -> str:
+    return load_library().bilogp_status_string(status).decode()
+
+
+def bilogp_last_error() -> str:
+    return load_library().bilogp_last_error().decode()
+
+
+# ---------------------------------------------------------------- forward calls
+def _bias_dtype(bias: Optional[torch.Tensor]) -> int:
+    if bias is None:
+        return BILOGP_BIAS_NONE
+    if bias.dtype == torch.bfloat16:
+        return BILOGP_BIAS_BF16
+    if bias.dtype == torch.float32:
+        return BILOGP_BIAS_F32
+    raise TypeError(f"bias must be bfloat16 or float32, got {bias.dtype}")
+
+
+def bilogp_forward(hidden: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
+                   bias: Optional[torch.Tensor], logp_out: torch.Tensor, lse_out: torch.Tensor,
+                   stream=None) -> None:
+    """``bilogp_forward`` on 2-D contiguous device tensors (hidden [N, H] bf16,
+    weight [V, H] bf16, target [N] int64, bias [V] fp32 or None, outputs [N]
+    fp32).  The library allocates its workspace stream-ordered."""
+    N, H = hidden.shape
+    V = weight.shape[0]
+    lib = load_library()
+    with torch.cuda.device(hidden.device):
+        st = lib.bilogp_forward(_ptr(hidden), _ptr(weight), _ptr(target), _ptr(bias),
+                                _ptr(logp_out), _ptr(lse_out), N, H, V,
+                                _stream_handle(stream, hidden.device))
+    _check(st)
+
+
+def bilogp_forward_ex(hidden: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
+                      bias: Optional[torch.Tensor], logp_out: torch.Tensor,
+                      lse_out: torch.Tensor, workspace: Optional[torch.Tensor],
+                      stream=None) -> None:
+    """``bilogp_forward_ex`` with a caller-owned workspace tensor (any dtype;
+    its byte size is passed).  Allocates nothing."""
+    N, H = hidden.shape
+    V = weight.shape[0]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib = load_library()
+    with torch.cuda.device(hidden.device):
+        st = lib.bilogp_forward_ex(_ptr(hidden), _ptr(weight), _ptr(target), _ptr(bias),
+                                   _bias_dtype(bias), _ptr(logp_out), _ptr(lse_out), N, H, V,
+                                   _ptr(workspace), ws_bytes,
+                                   _stream_handle(stream, hidden.device))
+    _check(st)
+
+
+def bilogp_partials(hidden: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
+                    bias: Optional[torch.Tensor], workspace: torch.Tensor, stream=None) -> None:
+    """``bilogp_partials``: projection + per-split online softmax into the
+    workspace (partials and target logits)."""
+    N, H = hidden.shape
+    V = weight.shape[0]
+    lib = load_library()
+    with torch.cuda.device(hidden.device):
+        st = lib.bilogp_partials(_ptr(hidden), _ptr(weight), _ptr(target), _ptr(bias),
+                                 _bias_dtype(bias), N, H, V, _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(),
+                                 _stream_handle(stream, hidden.device))
+    _check(st)
+
+
+def bilogp_merge(target: torch.Tensor, workspace: torch.Tensor, logp_out: torch.Tensor,
+                 lse_out: torch.Tensor, V: int, stream=None) -> None:
+    """``bilogp_merge``: ascending combine of the workspace partials."""
+    N = target.shape[0]
+    lib = load_library()
+    with torch.cuda.device(target.device):
+        st = lib.bilogp_merge(_ptr(target), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _ptr(logp_out),
+                              _ptr(lse_out), N, V, _stream_handle(stream, target.device))
+    _check(st)

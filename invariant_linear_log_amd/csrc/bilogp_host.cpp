@@ -1,0 +1,355 @@
+// C ABI of the batch-invariant fused linear log-probability forward:
+// argument validation (fail closed), the gfx950 gate, the V-only split
+// policy, workspace layout and the two launches.  Never synchronizes.
+//
+// RL-Kernel PR #337, "feat(linear-logp): add batch-invariant fused SM90
+// operator": the native entry point takes hidden, weight, target and an
+// optional bias and returns the log-probability and log-sum-exp (sequence
+// diagram); the split count comes from V only (annotation on
+// select_batch_invariant_vocab_splits); an unsupported platform is an
+// explicit error, never a generic fallback (annotation on the registry entry).
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+#include <string>
+
+#include "../../include/bilogp.h"
+#include "bilogp_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bilogp_status fail(bilogp_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+constexpr int64_t kMaxV = int64_t(1) << 30;
+constexpr int64_t kMaxH = int64_t(1) << 20;
+constexpr int64_t kMaxN = int64_t(1) << 32;
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// V rounded up to whole vocabulary tiles.
+size_t padded_vocab(int64_t V) {
+  return (size_t)((V + bilogp::kVtileCols - 1) / bilogp::kVtileCols) * bilogp::kVtileCols;
+}
+
+// Workspace layout: [N, S] float2 partials | [N] float target logits |
+// fp32 bias copy padded to whole tiles; each part 256-byte aligned.
+struct WsLayout {
+  float2* part;
+  float* tlogit;
+  float* bias32;
+};
+
+WsLayout ws_layout(void* ws, int64_t N, int S) {
+  char* b = static_cast<char*>(ws);
+  const size_t o1 = round_up((size_t)N * S * sizeof(float2));
+  const size_t o2 = o1 + round_up((size_t)N * sizeof(float));
+  return WsLayout{reinterpret_cast<float2*>(b), reinterpret_cast<float*>(b + o1),
+                  reinterpret_cast<float*>(b + o2)};
+}
+
+// Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+bilogp_status check_device(int* dev_out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0)
+    return fail(BILOGP_E_UNSUPPORTED, std::string("no usable HIP device: ") + hipGetErrorString(e));
+  if (dev >= kMaxDevices) return fail(BILOGP_E_UNSUPPORTED, "device index out of range");
+  int st = g_arch_ok[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(BILOGP_E_HIP, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
+    st = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch_ok[dev].store(st, std::memory_order_release);
+    if (st != 1)
+      return fail(BILOGP_E_UNSUPPORTED,
+                  std::string("device architecture is ") + prop.gcnArchName + ", need gfx950");
+  }
+  if (st != 1) return fail(BILOGP_E_UNSUPPORTED, "device architecture is not gfx950");
+  *dev_out = dev;
+  return BILOGP_OK;
+}
+
+bilogp_status check_on_device(const void* ptr, int dev, const char* name) {
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, ptr);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();   // clear the sticky error left by a host pointer
+    return fail(BILOGP_E_UNSUPPORTED, std::string(name) + " is not device memory");
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+    return fail(BILOGP_E_UNSUPPORTED, std::string(name) + " is not device memory");
+  if (attr.device != dev)
+    return fail(BILOGP_E_UNSUPPORTED, std::string(name) + " is on another device");
+  return BILOGP_OK;
+}
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+Range range_of(const void* p, size_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + bytes};
+}
+
+}  // namespace
+
+extern "C" {
+
+int bilogp_abi_version(void) { return BILOGP_ABI_VERSION; }
+
+int bilogp_vtile_cols(void) { return bilogp::kVtileCols; }
+
+int bilogp_max_splits(void) { return bilogp::kMaxSplits; }
+
+int bilogp_vtiles_per_split(int64_t V) {
+  if (V <= 0 || V > kMaxV) return 0;
+  const int64_t tiles = (V + bilogp::kVtileCols - 1) / bilogp::kVtileCols;
+  return (int)((tiles + bilogp::kMaxSplits - 1) / bilogp::kMaxSplits);
+}
+
+int bilogp_num_vocab_splits(int64_t V) {
+  const int per_split = bilogp_vtiles_per_split(V);
+  if (per_split == 0) return 0;
+  const int64_t tiles = (V + bilogp::kVtileCols - 1) / bilogp::kVtileCols;
+  return (int)((tiles + per_split - 1) / per_split);
+}
+
+size_t bilogp_workspace_bytes(int64_t N, int64_t V) {
+  const int S = bilogp_num_vocab_splits(V);
+  if (N < 0 || N > kMaxN || S == 0) return (size_t)-1;
+  if (N == 0) return 0;
+  return round_up((size_t)N * (size_t)S * sizeof(float2)) + round_up((size_t)N * sizeof(float)) +
+         round_up(padded_vocab(V) * sizeof(float));
+}
+
+const char* bilogp_status_string(int status) {
+  switch (status) {
+    case BILOGP_OK: return "ok";
+    case BILOGP_E_INVALID_ARG: return "invalid argument";
+    case BILOGP_E_UNSUPPORTED: return "unsupported request";
+    case BILOGP_E_WORKSPACE: return "workspace missing or too small";
+    case BILOGP_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* bilogp_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"
+
+namespace {
+
+// Which parts of the call are present: the projection needs the inputs, the
+// merge needs the outputs; both need target and the workspace.
+enum Part : int { kProj = 1, kMerge = 2 };
+
+struct Call {
+  const void* hidden;
+  const void* weight;
+  const int64_t* target;
+  const void* bias;
+  int bias_dtype;
+  float* logp;
+  float* lse;
+  int64_t N, H, V;
+  void* ws;
+  size_t ws_bytes;
+};
+
+// Full argument validation (fail closed) and the launch parameters.  Pure
+// host checks come first, then the device checks; nothing is launched here.
+bilogp_status validate(const Call& c, int parts, bilogp::ProjParams* out) {
+  const bool proj = parts & kProj, merge = parts & kMerge;
+  if (!c.target || (proj && (!c.hidden || !c.weight)) || (merge && (!c.logp || !c.lse)))
+    return fail(BILOGP_E_INVALID_ARG, "a required pointer is null");
+  if (c.N < 0 || c.N > kMaxN) return fail(BILOGP_E_INVALID_ARG, "N out of range [0, 2^32]");
+  if (proj && (c.H <= 0 || c.H > kMaxH))
+    return fail(BILOGP_E_INVALID_ARG, "H out of range [1, 2^20]");
+  if (c.V <= 0 || c.V > kMaxV) return fail(BILOGP_E_INVALID_ARG, "V out of range [1, 2^30]");
+  size_t bias_esz = 0;
+  if (proj) {
+    if (c.bias_dtype != BILOGP_BIAS_NONE && c.bias_dtype != BILOGP_BIAS_BF16 &&
+        c.bias_dtype != BILOGP_BIAS_F32)
+      return fail(BILOGP_E_UNSUPPORTED, "unknown bias dtype");
+    if ((c.bias_dtype == BILOGP_BIAS_NONE) != (c.bias == nullptr))
+      return fail(BILOGP_E_INVALID_ARG, "bias must be null exactly when bias_dtype is NONE");
+    if (c.H % 8 != 0) return fail(BILOGP_E_UNSUPPORTED, "H must be a multiple of 8");
+    if ((reinterpret_cast<uintptr_t>(c.hidden) | reinterpret_cast<uintptr_t>(c.weight)) % 16)
+      return fail(BILOGP_E_UNSUPPORTED, "hidden and weight must be 16-byte aligned");
+    bias_esz = c.bias_dtype == BILOGP_BIAS_F32 ? 4 : 2;
+    if (c.bias && reinterpret_cast<uintptr_t>(c.bias) % bias_esz != 0)
+      return fail(BILOGP_E_UNSUPPORTED, "bias is misaligned for its dtype");
+  }
+  if (reinterpret_cast<uintptr_t>(c.target) % 8 != 0)
+    return fail(BILOGP_E_UNSUPPORTED, "target must be 8-byte aligned");
+  if (merge && (reinterpret_cast<uintptr_t>(c.logp) | reinterpret_cast<uintptr_t>(c.lse)) % 4)
+    return fail(BILOGP_E_UNSUPPORTED, "outputs must be 4-byte aligned");
+  if (c.N == 0) return BILOGP_OK;
+
+  const int S = bilogp_num_vocab_splits(c.V);
+  const int64_t R = (c.N + bilogp::kBlockRows - 1) / bilogp::kBlockRows;
+  if (R * S > INT32_MAX) return fail(BILOGP_E_INVALID_ARG, "N too large for one launch");
+
+  if (merge) {
+    const Range r_logp = range_of(c.logp, (size_t)c.N * 4), r_lse = range_of(c.lse, (size_t)c.N * 4);
+    const Range others[] = {
+        proj ? range_of(c.hidden, (size_t)c.N * c.H * 2) : Range{0, 0},
+        proj ? range_of(c.weight, (size_t)c.V * c.H * 2) : Range{0, 0},
+        range_of(c.target, (size_t)c.N * 8),
+        (proj && c.bias) ? range_of(c.bias, (size_t)c.V * bias_esz) : Range{0, 0},
+        c.ws ? range_of(c.ws, c.ws_bytes) : Range{0, 0}};
+    if (overlap(r_logp, r_lse)) return fail(BILOGP_E_INVALID_ARG, "logp_out and lse_out overlap");
+    for (const Range& in : others)
+      if (overlap(r_logp, in) || overlap(r_lse, in))
+        return fail(BILOGP_E_INVALID_ARG, "an output overlaps an input or the workspace");
+  }
+
+  const size_t need = bilogp_workspace_bytes(c.N, c.V);
+  if (!c.ws || c.ws_bytes < need)
+    return fail(BILOGP_E_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
+  if (reinterpret_cast<uintptr_t>(c.ws) % kAlign != 0)
+    return fail(BILOGP_E_WORKSPACE, "workspace must be 256-byte aligned");
+
+  int dev = -1;
+  bilogp_status st = check_device(&dev);
+  if (st != BILOGP_OK) return st;
+  const void* ptrs[] = {proj ? c.hidden : nullptr, proj ? c.weight : nullptr, c.target,
+                        proj ? c.bias : nullptr, merge ? c.logp : nullptr,
+                        merge ? c.lse : nullptr, c.ws};
+  const char* names[] = {"hidden", "weight", "target", "bias", "logp_out", "lse_out", "workspace"};
+  for (int i = 0; i < 7; ++i) {
+    if (!ptrs[i]) continue;
+    st = check_on_device(ptrs[i], dev, names[i]);
+    if (st != BILOGP_OK) return st;
+  }
+
+  const WsLayout L = ws_layout(c.ws, c.N, S);
+  bilogp::ProjParams& p = *out;
+  p.hidden = c.hidden;
+  p.weight = c.weight;
+  p.target = c.target;
+  p.bias = c.bias ? L.bias32 : nullptr;   // the kernel reads the padded fp32 copy
+  p.part = L.part;
+  p.tlogit = L.tlogit;
+  p.N = c.N;
+  p.H = (int32_t)c.H;
+  p.V = (int32_t)c.V;
+  p.bias_kind = c.bias_dtype == BILOGP_BIAS_BF16 ? bilogp::kBiasBf16
+                : c.bias_dtype == BILOGP_BIAS_F32 ? bilogp::kBiasF32
+                                                  : bilogp::kBiasNone;
+  p.T = (int32_t)((c.V + bilogp::kVtileCols - 1) / bilogp::kVtileCols);
+  p.vps = bilogp_vtiles_per_split(c.V);
+  p.S = S;
+  p.R = (int32_t)R;
+  return BILOGP_OK;
+}
+
+bilogp_status launch(const bilogp::ProjParams& p, const Call& c, int parts, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* logp = c.logp;
+  float* lse = c.lse;
+  if ((parts & kProj) && c.bias) {
+    hipError_t e = bilogp::launch_bias_f32(c.bias, p.bias_kind, p.V,
+                                           const_cast<float*>(static_cast<const float*>(p.bias)), s);
+    if (e != hipSuccess)
+      return fail(BILOGP_E_HIP, std::string("bias copy launch: ") + hipGetErrorString(e));
+  }
+  if (parts & kProj) {
+    hipError_t e = bilogp::launch_proj_lse(p, s);
+    if (e != hipSuccess)
+      return fail(BILOGP_E_HIP, std::string("projection launch: ") + hipGetErrorString(e));
+  }
+  if (parts & kMerge) {
+    hipError_t e = bilogp::launch_merge(p.part, p.tlogit, p.target, logp, lse, p.N, p.S, p.V, s);
+    if (e != hipSuccess)
+      return fail(BILOGP_E_HIP, std::string("merge launch: ") + hipGetErrorString(e));
+  }
+  return BILOGP_OK;
+}
+
+bilogp_status run(const Call& c, int parts, void* stream) {
+  g_last_error.clear();
+  bilogp::ProjParams p;
+  bilogp_status st = validate(c, parts, &p);
+  if (st != BILOGP_OK || c.N == 0) return st;
+  return launch(p, c, parts, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+bilogp_status bilogp_forward_ex(const void* hidden, const void* weight, const int64_t* target,
+                                const void* bias, int bias_dtype, float* logp_out,
+                                float* lse_out, int64_t N, int64_t H, int64_t V,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  const Call c{hidden, weight, target, bias, bias_dtype, logp_out, lse_out,
+               N,      H,      V,      workspace, workspace_bytes};
+  return run(c, kProj | kMerge, stream);
+}
+
+bilogp_status bilogp_partials(const void* hidden, const void* weight, const int64_t* target,
+                              const void* bias, int bias_dtype, int64_t N, int64_t H, int64_t V,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  const Call c{hidden, weight, target, bias, bias_dtype, nullptr, nullptr,
+               N,      H,      V,      workspace, workspace_bytes};
+  return run(c, kProj, stream);
+}
+
+bilogp_status bilogp_merge(const int64_t* target, const void* workspace, size_t workspace_bytes,
+                           float* logp_out, float* lse_out, int64_t N, int64_t V, void* stream) {
+  const Call c{nullptr, nullptr, target, nullptr, BILOGP_BIAS_NONE, logp_out, lse_out,
+               N,       8,       V,      const_cast<void*>(workspace), workspace_bytes};
+  return run(c, kMerge, stream);
+}
+
+bilogp_status bilogp_forward(const void* hidden, const void* weight, const int64_t* target,
+                             const float* bias, float* logp_out, float* lse_out, int64_t N,
+                             int64_t H, int64_t V, void* stream) {
+  g_last_error.clear();
+  const size_t need = bilogp_workspace_bytes(N, V);
+  if (need == (size_t)-1) {
+    // let the full validation report the precise reason
+    return bilogp_forward_ex(hidden, weight, target, bias,
+                             bias ? BILOGP_BIAS_F32 : BILOGP_BIAS_NONE, logp_out, lse_out, N, H,
+                             V, nullptr, 0, stream);
+  }
+  if (need == 0)
+    return bilogp_forward_ex(hidden, weight, target, bias,
+                             bias ? BILOGP_BIAS_F32 : BILOGP_BIAS_NONE, logp_out, lse_out, N, H,
+                             V, nullptr, 0, stream);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, need, s);
+  if (e != hipSuccess)
+    return fail(BILOGP_E_HIP, std::string("hipMallocAsync: ") + hipGetErrorString(e));
+  bilogp_status st = bilogp_forward_ex(hidden, weight, target, bias,
+                                       bias ? BILOGP_BIAS_F32 : BILOGP_BIAS_NONE, logp_out,
+                                       lse_out, N, H, V, ws, need, stream);
+  std::string keep = g_last_error;
+  e = hipFreeAsync(ws, s);
+  if (st != BILOGP_OK) return fail(st, keep);
+  if (e != hipSuccess)
+    return fail(BILOGP_E_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(e));
+  return BILOGP_OK;
+}
+
+}  // extern "C"

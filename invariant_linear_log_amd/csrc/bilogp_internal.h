@@ -1,0 +1,50 @@
+// Internal declarations shared by the host library and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bilogp {
+
+// Part of the bit contract: the vocabulary tile width and the largest split
+// count decide which columns are reduced together and in which order.
+constexpr int kVtileCols = 256;
+constexpr int kMaxSplits = 64;
+
+// Tokens handled by one projection workgroup.  Internal only: a row's
+// arithmetic does not depend on it (no reduction mixes rows).
+constexpr int kBlockRows = 256;
+
+enum BiasKind : int32_t { kBiasNone = 0, kBiasBf16 = 1, kBiasF32 = 2 };
+
+struct ProjParams {
+  const void* hidden;      // bf16 [N, H], row-major
+  const void* weight;      // bf16 [V, H], row-major
+  const int64_t* target;   // [N]
+  const void* bias;        // fp32 [ceil(V / kVtileCols) * kVtileCols] or null
+  float2* part;            // [N, S]: per (row, split) running max and sum of exp(z - max)
+  float* tlogit;           // [N]: logit of each row's target
+  int64_t N;
+  int32_t H;
+  int32_t V;
+  int32_t bias_kind;
+  int32_t T;               // vocabulary tiles, ceil(V / kVtileCols)
+  int32_t vps;             // tiles per split
+  int32_t S;               // splits
+  int32_t R;               // row blocks, ceil(N / kBlockRows)
+};
+
+// Enqueue the exact fp32 copy of a bf16 / fp32 bias, zero-padded to whole
+// vocabulary tiles (out holds ceil(V / kVtileCols) * kVtileCols floats).
+hipError_t launch_bias_f32(const void* bias, int32_t kind, int32_t V, float* out,
+                           hipStream_t stream);
+
+// Enqueue the fused projection + per-split online-softmax kernel.
+hipError_t launch_proj_lse(const ProjParams& p, hipStream_t stream);
+
+// Enqueue the ascending split merge: lse and logp per row.
+hipError_t launch_merge(const float2* part, const float* tlogit, const int64_t* target,
+                        float* logp, float* lse, int64_t N, int32_t S, int32_t V,
+                        hipStream_t stream);
+
+}  // namespace bilogp

@@ -1,0 +1,424 @@
+// Fused projection + per-split online softmax for gfx950 (CDNA4).
+//
+// Operation (RL-Kernel PR #337, "feat(linear-logp): add batch-invariant fused
+// SM90 operator", description): logits z = hidden . W^T (+ bias) are formed
+// tile by tile and never stored; every (row block, vocabulary split) pair
+// reduces its split's contiguous vocabulary tiles, in ascending order, to a
+// per-row online-softmax partial (running max m, sum s of exp(z - m)).  The
+// partials are merged by merge.hip.
+//
+// Workgroup: 512 threads (8 wave64s), one (row block of 256 tokens, split).
+// Per vocabulary tile of 256 columns the workgroup computes the 256 x 256
+// product W_tile[256, H] . hidden_block[256, H]^T with
+// v_mfma_f32_32x32x16_bf16, W as the A operand (MFMA rows = vocabulary) and
+// hidden as the B operand (MFMA columns = tokens).  In that orientation each
+// lane's accumulators hold ONE token column and 64 vocabulary rows, so the
+// per-token max / sum-exp over a tile is mostly a sequential, lane-local loop
+// whose order is fixed by the tile geometry alone.
+//
+// Waves: w = 2 * wt + wv.  wv in {0, 1} picks vocabulary rows [128 wv, +128)
+// of the tile, wt in {0..3} picks tokens [64 wt, +64) of the block.  A wave
+// holds 4 x 2 MFMA tiles of 32 x 32 (128 accumulator registers per lane).
+//
+// Bit contract.  For a fixed (token, vocabulary column) the K reduction is
+// the same chain of MFMA instructions over ascending 16-wide K steps
+// whatever N or the token's slot in the block; the per-token reductions over
+// vocabulary columns follow the (lane, register) layout of the tile, which
+// is the same for every token column; the cross-lane and cross-wave merges
+// use fixed operand order.  Nothing depends on N, the row block or the
+// number of compute units.
+//
+// Memory pipeline.  K is staged in 32-wide slices through a ring of four LDS
+// stages (32 KB each: a 256 x 32 W slice and a 256 x 32 hidden slice).
+// Slices are fetched with buffer loads that write LDS directly (no VGPR
+// round trip), three stages ahead of the MFMAs.  Out-of-range rows (the
+// vocabulary tail, the last row block) and K chunks past H read as zero
+// through the buffer descriptors' range check.  Inside a stage each 256 x 32
+// slice is stored as 256 rows of four 16-byte chunks, with chunk c of row r
+// at position c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3: the MFMA operand
+// reads (32 rows x 2 chunks per instruction) then touch distinct banks.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "bilogp_internal.h"
+
+namespace bilogp {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kThreads = 512;
+constexpr int kBK = 32;                            // K per stage
+constexpr int kStages = 4;
+constexpr int kTileBytes = kVtileCols * kBK * 2;   // 16 KB: one operand slice
+constexpr int kSlotBytes = 2 * kTileBytes + kVtileCols * 4;  // W, hidden, bias
+constexpr int kLdsRowBytes = kBK * 2;              // 64 B per slice row
+constexpr uint32_t kOutOfRange = 0x7ffffff0u;      // any offset past num_records
+constexpr int kRsrcWord3 = 0x00020000;             // gfx9 raw buffer, 32-bit data
+constexpr float kLog2e = 1.4426950408889634f;
+
+static_assert(kBlockRows == 256 && kVtileCols == 256, "tile geometry is fixed");
+
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Merge of two online-softmax states (lo from the lower vocabulary columns).
+__device__ __forceinline__ void merge_state(float m_lo, float s_lo, float m_hi, float s_hi,
+                                            float& m, float& s) {
+  const float M = fmaxf(m_lo, m_hi);
+  const float mu = (M == -INFINITY) ? 0.f : M;
+  s = s_lo * exp2_hw((m_lo - mu) * kLog2e) + s_hi * exp2_hw((m_hi - mu) * kLog2e);
+  m = M;
+}
+
+template <int I>
+using Slot = std::integral_constant<int, I>;
+
+__global__ __launch_bounds__(kThreads, 1) void proj_lse_kernel(const ProjParams p) {
+  // Four ring slots, each its own LDS variable, so the compiler can tell a
+  // read of one slot from a direct-to-LDS load into another and does not
+  // drain the load pipeline before every read.  Slot layout: W slice (16 KB),
+  // hidden slice (16 KB), bias of the tile (1 KB, last slot only).
+  __shared__ __attribute__((aligned(1024))) uint8_t slot0[kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot1[kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot2[kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot3[kSlotBytes];
+  __shared__ float2 red[kBlockRows];
+
+  auto slot_ptr = [&](auto sc) -> uint8_t* {
+    constexpr int I = decltype(sc)::value;
+    if constexpr (I == 0) return slot0;
+    else if constexpr (I == 1) return slot1;
+    else if constexpr (I == 2) return slot2;
+    else return slot3;
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wv = wave & 1;
+  const int wt = wave >> 1;
+  const int half = lane >> 5;
+
+  // Block id -> (split, row block).  Blocks are handed to the eight XCDs
+  // round-robin; give each XCD a contiguous run of (split-major) tiles so the
+  // row blocks sharing a W slice share that XCD's L2.  A bijection.
+  const int nblk = p.R * p.S;
+  const int per_xcd = nblk >> 3;
+  int u = blockIdx.x;
+  if (u < (per_xcd << 3)) u = (u & 7) * per_xcd + (u >> 3);
+  const int split = u / p.R;
+  const int rb = u - split * p.R;
+
+  const int64_t m0 = (int64_t)rb * kBlockRows;
+  const int rows_here = (int)min((int64_t)kBlockRows, p.N - m0);
+  const int vt_begin = split * p.vps;
+  const int nvt = min(vt_begin + p.vps, p.T) - vt_begin;
+  const int H = p.H;
+  // K stages per tile, padded to a multiple of the ring size with stages that
+  // read only zeros (they leave the accumulators unchanged), so every tile
+  // starts in slot 0 and ends in slot 3.
+  const int KT = ((H + kBK - 1) / kBK + kStages - 1) / kStages * kStages;
+  const int G = nvt * KT;                          // stages in this workgroup
+
+  // ---- per-lane load descriptors: 4 direct-to-LDS loads per stage --------
+  // Instruction j of wave `wave` fills slots [(2 wave + j) * 64, +64) of the
+  // W slice and of the hidden slice: 16 rows x 4 chunks of 16 bytes.
+  uint32_t voff_base[2];
+  int kchunk[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = (wave * 2 + j) * 16 + (lane >> 2);
+    const int cc = (lane & 3) ^ swz(r);
+    voff_base[j] = (uint32_t)r * (uint32_t)H * 2u + (uint32_t)cc * 16u;
+    kchunk[j] = cc * 8;
+  }
+  const __amdgpu_buffer_rsrc_t rsrc_h = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const uint16_t*)p.hidden + m0 * H), (short)0, rows_here * H * 2, kRsrcWord3);
+
+  // ---- per-lane LDS read offsets for the MFMA operands ----------------------
+  // A (W): row wv*128 + vi*32 + (lane & 31), K chunk 2u + half; vi adds 2 KB.
+  // B (hidden): row wt*64 + ti*32 + (lane & 31); ti adds 2 KB.
+  const int fr = swz(lane & 31);
+  int a_off[2], b_off[2];
+#pragma unroll
+  for (int uu = 0; uu < 2; ++uu) {
+    const int c = (2 * uu + half) ^ fr;
+    a_off[uu] = ((wv * 128 + (lane & 31)) * 4 + c) * 16;
+    b_off[uu] = kTileBytes + ((wt * 64 + (lane & 31)) * 4 + c) * 16;
+  }
+
+  // ---- targets of this lane's two token columns ------------------------------
+  int64_t tgt[2];
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti) {
+    const int j = wt * 64 + ti * 32 + (lane & 31);
+    tgt[ti] = (j < rows_here) ? p.target[m0 + j] : (int64_t)-1;
+  }
+
+  // Issue the direct-to-LDS loads of stage g into ring slot SC.
+  auto issue = [&](int g, auto sc) {
+    constexpr int I = decltype(sc)::value;
+    if (g >= G) return;
+    const int v = g / KT;
+    const int kt = g - v * KT;
+    const int k0 = kt * kBK;
+    const int vbase = (vt_begin + v) * kVtileCols;
+    const int vrows = min(kVtileCols, p.V - vbase);
+    uint8_t* st = slot_ptr(sc);
+    const __amdgpu_buffer_rsrc_t rsrc_w = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint16_t*)p.weight + (int64_t)vbase * H), (short)0, vrows * H * 2,
+        kRsrcWord3);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bool ok = k0 + kchunk[j] < H;
+      const uint32_t voff = ok ? voff_base[j] + (uint32_t)k0 * 2u : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc_w, (lds_void*)(st + (wave * 2 + j) * 1024), 16, voff, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bool ok = k0 + kchunk[j] < H;
+      const uint32_t voff = ok ? voff_base[j] + (uint32_t)k0 * 2u : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc_h, (lds_void*)(st + kTileBytes + (wave * 2 + j) * 1024), 16, voff, 0, 0, 0);
+    }
+    if constexpr (I == kStages - 1) {
+      // the tile's bias rides with its last stage, whose slot is still intact
+      // when the tile's epilogue runs; the bias copy is fp32 and padded to
+      // whole tiles, so all 64 lanes' 16-byte chunks are in range
+      if (p.bias_kind != kBiasNone && wave == 0) {
+        const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)((const float*)p.bias + vbase), (short)0, kVtileCols * 4, kRsrcWord3);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_b, (lds_void*)(st + 2 * kTileBytes), 16,
+                                                 (uint32_t)lane * 16u, 0, 0, 0);
+      }
+    }
+  };
+
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int vi = 0; vi < 4; ++vi)
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) acc[vi][ti] = floatx16{};
+
+  // MFMAs of the stage held in ring slot SC.
+  auto compute = [&](auto sc) {
+    const uint8_t* st = slot_ptr(sc);
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu) {
+      bf16x8 a[4], b[2];
+#pragma unroll
+      for (int vi = 0; vi < 4; ++vi)
+        a[vi] = *(const bf16x8*)(st + a_off[uu] + vi * 32 * kLdsRowBytes);
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+        b[ti] = *(const bf16x8*)(st + b_off[uu] + ti * 32 * kLdsRowBytes);
+#pragma unroll
+      for (int vi = 0; vi < 4; ++vi)
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti)
+          acc[vi][ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[vi], b[ti], acc[vi][ti], 0, 0, 0);
+    }
+  };
+
+  // Wait for this wave's loads of stage g, then barrier: afterwards every
+  // wave's stage-g data is in LDS and nobody still reads the slot of stage
+  // g - 1.  Younger stages stay in flight: each is at least four load
+  // instructions per wave, so "at most 4 * younger outstanding" suffices.  The
+  // barrier is a bare s_barrier (the compiler-level memory clobber keeps LDS
+  // accesses on their side of it); a C++ workgroup fence here would drain
+  // every in-flight load.
+  auto sync_stage = [&](auto younger_c, int g) {
+    constexpr int Y = decltype(younger_c)::value;
+    if constexpr (Y >= 2) {
+      wait_vmcnt<8>();
+    } else {
+      // only the last group of four stages has fewer younger stages
+      if (g + kStages < G) {
+        wait_vmcnt<8>();
+      } else if constexpr (Y == 1) {
+        wait_vmcnt<4>();
+      } else {
+        wait_vmcnt<0>();
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float s_run[2] = {0.f, 0.f};
+
+  issue(0, Slot<0>{});
+  issue(1, Slot<1>{});
+  issue(2, Slot<2>{});
+
+  // G is a multiple of four: stages g .. g+3 live in slots 0 .. 3.
+  for (int g = 0; g < G; g += kStages) {
+    sync_stage(Slot<2>{}, g);
+    issue(g + 3, Slot<3>{});
+    compute(Slot<0>{});
+    sync_stage(Slot<2>{}, g + 1);
+    issue(g + 4, Slot<0>{});
+    compute(Slot<1>{});
+    sync_stage(Slot<1>{}, g);
+    issue(g + 5, Slot<1>{});
+    compute(Slot<2>{});
+    sync_stage(Slot<0>{}, g);
+    issue(g + 6, Slot<2>{});
+    compute(Slot<3>{});
+
+    const int v = g / KT;
+    if (g + kStages != (v + 1) * KT) continue;
+
+    // ---- epilogue of vocabulary tile v -------------------------------------
+    // acc[vi][ti][r] holds z for token column wt*64 + ti*32 + (lane & 31) and
+    // vocabulary row wv*128 + vi*32 + 8*(r/4) + 4*half + (r%4) of the tile.
+    const int vbase = (vt_begin + v) * kVtileCols;
+    const int vw = vbase + wv * 128;               // first column of this wave
+    if (p.bias_kind != kBiasNone) {
+      const uint8_t* braw = slot3 + 2 * kTileBytes;
+#pragma unroll
+      for (int vi = 0; vi < 4; ++vi)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c0 = wv * 128 + vi * 32 + 8 * q + 4 * half;
+          const floatx4 bb = *(const floatx4*)(braw + c0 * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[vi][0][4 * q + e] += bb[e];
+            acc[vi][1][4 * q + e] += bb[e];
+          }
+        }
+    }
+    if (vbase + kVtileCols > p.V) {                // vocabulary tail: mask columns >= V
+#pragma unroll
+      for (int vi = 0; vi < 4; ++vi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int col = vw + vi * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (col >= p.V) {
+            acc[vi][0][r] = -INFINITY;
+            acc[vi][1][r] = -INFINITY;
+          }
+        }
+    }
+
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) {
+      // target capture: exactly one (tile, lane, register) in the grid holds it
+      const int64_t rel64 = tgt[ti] - vw;
+      const int rel = (int)rel64;
+      const bool hit = rel64 >= 0 && rel64 < 128 && ((rel >> 2) & 1) == half;
+      if (__any(hit)) {
+        const int vi_t = rel >> 5;
+        const int r_t = ((rel >> 3) & 3) * 4 + (rel & 3);
+        float val = 0.f;
+#pragma unroll
+        for (int vi = 0; vi < 4; ++vi)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (vi == vi_t && r == r_t) val = acc[vi][ti][r];
+        if (hit) p.tlogit[m0 + wt * 64 + ti * 32 + (lane & 31)] = val;
+      }
+
+      // online softmax over this lane's 64 values of the tile
+      float mx = acc[0][ti][0];
+#pragma unroll
+      for (int vi = 0; vi < 4; ++vi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[vi][ti][r]);
+      const float m_new = fmaxf(m_run[ti], mx);
+      const float mu = (m_new == -INFINITY) ? 0.f : m_new;
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int vi = 0; vi < 4; ++vi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ps[r & 3] += exp2_hw((acc[vi][ti][r] - mu) * kLog2e);
+      const float tile_sum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      s_run[ti] = s_run[ti] * exp2_hw((m_run[ti] - mu) * kLog2e) + tile_sum;
+      m_run[ti] = m_new;
+    }
+#pragma unroll
+    for (int vi = 0; vi < 4; ++vi)
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti) acc[vi][ti] = floatx16{};
+  }
+
+  // ---- split done: merge lane halves, then the two vocabulary-half waves ----
+  float mm[2], ss[2];
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti) {
+    const float om = __shfl_xor(m_run[ti], 32);
+    const float os = __shfl_xor(s_run[ti], 32);
+    if (half == 0)
+      merge_state(m_run[ti], s_run[ti], om, os, mm[ti], ss[ti]);
+    else
+      merge_state(om, os, m_run[ti], s_run[ti], mm[ti], ss[ti]);
+  }
+  if (wv == 1 && half == 0) {
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) red[wt * 64 + ti * 32 + lane] = make_float2(mm[ti], ss[ti]);
+  }
+  __syncthreads();
+  if (wv == 0 && half == 0) {
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) {
+      const int j = wt * 64 + ti * 32 + lane;
+      const float2 hi = red[j];
+      float m, s;
+      merge_state(mm[ti], ss[ti], hi.x, hi.y, m, s);
+      if (j < rows_here) p.part[(m0 + j) * p.S + split] = make_float2(m, s);
+    }
+  }
+}
+
+// Exact fp32 copy of the bias (bf16 widens exactly), zero-padded to whole
+// vocabulary tiles so the projection kernel reads it in full 16-byte chunks.
+__global__ __launch_bounds__(256) void bias_to_f32_kernel(const void* __restrict__ bias,
+                                                          int32_t kind, int32_t V,
+                                                          int32_t padded, float* __restrict__ out) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= padded) return;
+  float v = 0.f;
+  if (c < V) {
+    v = (kind == kBiasF32) ? ((const float*)bias)[c]
+                           : __uint_as_float((uint32_t)((const uint16_t*)bias)[c] << 16);
+  }
+  out[c] = v;
+}
+
+}  // namespace
+
+hipError_t launch_bias_f32(const void* bias, int32_t kind, int32_t V, float* out,
+                           hipStream_t stream) {
+  const int32_t padded = (V + kVtileCols - 1) / kVtileCols * kVtileCols;
+  hipLaunchKernelGGL(bias_to_f32_kernel, dim3((unsigned)(padded / 256)), dim3(256), 0, stream,
+                     bias, kind, V, padded, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_proj_lse(const ProjParams& p, hipStream_t stream) {
+  const int64_t blocks = (int64_t)p.R * p.S;
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(proj_lse_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace bilogp

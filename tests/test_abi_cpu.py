@@ -1,0 +1,189 @@
+"""CPU checks of the C ABI (no kernel launches): the library loads, exports
+every function include/bilogp.h declares, its V-only split policy agrees with
+the oracle's independent reading of the page, and every fail-closed argument
+check fires before any device work."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import invariant_linear_log_amd as ila
+import oracle
+from invariant_linear_log_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bilogp.h")
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bilogp_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ila.load_library()
+    names = _header_functions()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in bilogp.h but not exported"
+        assert name in B.SIGNATURES, f"{name} has no binding signature"
+    assert set(B.SIGNATURES) == set(names)
+
+
+def test_constants_and_version():
+    assert ila.bilogp_abi_version() == 1
+    assert ila.bilogp_vtile_cols() == 256
+    assert ila.bilogp_max_splits() == 64
+    for s in range(5):
+        assert ila.bilogp_status_string(s) != "unknown status"
+    assert ila.bilogp_status_string(99) == "unknown status"
+
+
+def _policy_values():
+    vs = list(range(1, 5000, 13)) + [16383, 16384, 16385, 32000, 65536, 128256, 151936, 152064,
+                                      256 * 64 * 7 + 1, 10 ** 6, 2 ** 30]
+    return vs
+
+
+def test_split_policy_matches_oracle():
+    vt, mx = ila.bilogp_vtile_cols(), ila.bilogp_max_splits()
+    for V in _policy_values():
+        ranges = oracle.vocab_splits(V, vt, mx)
+        assert ila.bilogp_num_vocab_splits(V) == len(ranges), V
+        assert ila.bilogp_vtiles_per_split(V) == ranges[0][1] - ranges[0][0], V
+
+
+def test_split_policy_out_of_range():
+    for V in (0, -1, 2 ** 30 + 1, 2 ** 40):
+        assert ila.bilogp_num_vocab_splits(V) == 0
+        assert ila.bilogp_vtiles_per_split(V) == 0
+
+
+def test_workspace_bytes():
+    def up(x):
+        return (x + 255) // 256 * 256
+    for N, V in [(1, 1000), (8, 1000), (4096, 128256), (4097, 151936), (16384, 152064)]:
+        S = ila.bilogp_num_vocab_splits(V)
+        padded = (V + 255) // 256 * 256
+        assert ila.bilogp_workspace_bytes(N, V) == up(8 * N * S) + up(4 * N) + up(4 * padded)
+    assert ila.bilogp_workspace_bytes(0, 1000) == 0
+    big = (1 << 64) - 1
+    assert ila.bilogp_workspace_bytes(-1, 1000) == big
+    assert ila.bilogp_workspace_bytes(8, 0) == big
+
+
+# ------------------------------------------------------------- fail-closed checks
+FAKE = 0x10000          # aligned, never dereferenced: the checks below fail first
+
+
+def _call_ex(hidden=FAKE, weight=FAKE + 0x100000, target=FAKE + 0x200000, bias=None,
+             bias_dtype=0, logp=FAKE + 0x300000, lse=FAKE + 0x400000, N=8, H=64, V=1000,
+             ws=FAKE + 0x500000, ws_bytes=1 << 20):
+    lib = ila.load_library()
+    return lib.bilogp_forward_ex(hidden, weight, target, bias, bias_dtype, logp, lse, N, H, V,
+                                 ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=None), B.BILOGP_E_INVALID_ARG),
+    (dict(weight=None), B.BILOGP_E_INVALID_ARG),
+    (dict(target=None), B.BILOGP_E_INVALID_ARG),
+    (dict(logp=None), B.BILOGP_E_INVALID_ARG),
+    (dict(lse=None), B.BILOGP_E_INVALID_ARG),
+    (dict(N=-1), B.BILOGP_E_INVALID_ARG),
+    (dict(H=0), B.BILOGP_E_INVALID_ARG),
+    (dict(H=(1 << 20) + 8), B.BILOGP_E_INVALID_ARG),
+    (dict(V=0), B.BILOGP_E_INVALID_ARG),
+    (dict(V=(1 << 30) + 1), B.BILOGP_E_INVALID_ARG),
+    (dict(bias_dtype=7, bias=FAKE + 0x600000), B.BILOGP_E_UNSUPPORTED),
+    (dict(bias_dtype=2), B.BILOGP_E_INVALID_ARG),            # dtype without pointer
+    (dict(bias=FAKE + 0x600000), B.BILOGP_E_INVALID_ARG),    # pointer without dtype
+    (dict(H=60), B.BILOGP_E_UNSUPPORTED),                     # H % 8 != 0
+    (dict(hidden=FAKE + 8), B.BILOGP_E_UNSUPPORTED),          # misaligned
+    (dict(weight=FAKE + 0x100004), B.BILOGP_E_UNSUPPORTED),
+    (dict(target=FAKE + 0x200004), B.BILOGP_E_UNSUPPORTED),
+    (dict(bias_dtype=2, bias=FAKE + 0x600002), B.BILOGP_E_UNSUPPORTED),
+    (dict(logp=FAKE + 0x300002), B.BILOGP_E_UNSUPPORTED),
+    (dict(lse=FAKE + 0x300000), B.BILOGP_E_INVALID_ARG),      # outputs alias
+    (dict(lse=FAKE + 0x300010), B.BILOGP_E_INVALID_ARG),      # outputs overlap
+    (dict(logp=FAKE), B.BILOGP_E_INVALID_ARG),                # output aliases hidden
+    (dict(logp=FAKE + 0x200000), B.BILOGP_E_INVALID_ARG),     # output aliases target
+    (dict(logp=FAKE + 0x500000), B.BILOGP_E_INVALID_ARG),     # output aliases workspace
+    (dict(ws=None), B.BILOGP_E_WORKSPACE),
+    (dict(ws_bytes=100), B.BILOGP_E_WORKSPACE),
+    (dict(ws=FAKE + 0x500010), B.BILOGP_E_WORKSPACE),         # misaligned workspace
+])
+def test_forward_ex_fails_closed(kw, status):
+    st = _call_ex(**kw)
+    assert st == status, (st, ila.bilogp_last_error())
+    assert ila.bilogp_last_error() != ""
+
+
+def test_empty_batch_is_a_noop():
+    assert _call_ex(N=0, ws=None, ws_bytes=0) == B.BILOGP_OK
+    lib = ila.load_library()
+    assert lib.bilogp_forward(FAKE, FAKE + 0x100000, FAKE + 0x200000, None, FAKE + 0x300000,
+                              FAKE + 0x400000, 0, 64, 1000, None) == B.BILOGP_OK
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU path")
+def test_no_device_is_unsupported():
+    # valid arguments on a host without a gfx950 device: fail closed, no fallback
+    assert _call_ex() == B.BILOGP_E_UNSUPPORTED
+    assert "device" in ila.bilogp_last_error()
+
+
+def test_wrapper_rejects_requires_grad():
+    h = torch.zeros(4, 64, dtype=torch.bfloat16, requires_grad=True)
+    w = torch.zeros(100, 64, dtype=torch.bfloat16)
+    t = torch.zeros(4, dtype=torch.int64)
+    with pytest.raises(RuntimeError, match="forward-only"):
+        ila.forward(h, w, t)
+    wb = torch.zeros(100, 64, dtype=torch.bfloat16, requires_grad=True)
+    with pytest.raises(RuntimeError, match="forward-only"):
+        ila.forward(h.detach(), wb, t)
+    b = torch.zeros(100, requires_grad=True)
+    with pytest.raises(RuntimeError, match="forward-only"):
+        ila.forward(h.detach(), w, t, b)
+    # under no_grad the gate lets the call through to the device check
+    with torch.no_grad():
+        with pytest.raises(ValueError, match="GPU"):
+            ila.forward(h, w, t)
+
+
+@pytest.mark.parametrize("case", ["dtype_h", "dtype_t", "shape_h", "shape_t", "bias_shape",
+                                  "bias_dtype", "cpu"])
+def test_wrapper_rejects_bad_inputs(case):
+    h = torch.zeros(2, 3, 64, dtype=torch.bfloat16)
+    w = torch.zeros(100, 64, dtype=torch.bfloat16)
+    t = torch.zeros(2, 3, dtype=torch.int64)
+    b = None
+    exc = ValueError
+    if case == "dtype_h":
+        h, exc = h.float(), TypeError
+    elif case == "dtype_t":
+        t, exc = t.int(), TypeError
+    elif case == "shape_h":
+        h = torch.zeros(2, 3, 32, dtype=torch.bfloat16)
+    elif case == "shape_t":
+        t = torch.zeros(6, dtype=torch.int64)
+    elif case == "bias_shape":
+        b = torch.zeros(99)
+    elif case == "bias_dtype":
+        b, exc = torch.zeros(100, dtype=torch.float64), TypeError
+    with pytest.raises(exc):
+        ila.forward(h, w, t, b)
+
+
+def test_binding_raises_when_library_missing(tmp_path):
+    saved = B._lib
+    try:
+        B._lib = None
+        with pytest.raises(RuntimeError, match="missing"):
+            B.load_library(str(tmp_path / "libbilogp.so"))
+    finally:
+        B._lib = saved

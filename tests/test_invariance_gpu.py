@@ -1,0 +1,119 @@
+"""Bitwise batch invariance of the HIP path (torch.equal, never allclose):
+the full batch equals every concatenation of row-chunked runs; a row's bits do
+not depend on its slot, its neighbours, the tensor layout, the stream or the
+run.  RL-Kernel PR #337, description (tests paragraph and "What this PR
+changes"): same row + same V -> same arithmetic order and bits; the
+annotation on the chunk test: full-batch bits equal concatenated chunk bits.
+"""
+
+import pytest
+import torch
+
+import invariant_linear_log_amd as ila
+import synth
+from gpu_common import DEV, flat, run_ex, run_inputs, say
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}
+
+
+def sweep_inputs():
+    if "sweep" not in _CACHE:
+        inp = synth.make_inputs("sweep", device=DEV)
+        logp, lse = run_inputs(inp)
+        torch.cuda.synchronize()
+        _CACHE["sweep"] = (inp, logp, lse)
+    return _CACHE["sweep"]
+
+
+@pytest.mark.parametrize("chunk", [1, 7, 64, 1000, 4096])
+def test_chunked_equals_full(chunk):
+    inp, full_lp, full_ls = sweep_inputs()
+    h, t = flat(inp)
+    N = h.shape[0]
+    say(f"sweep chunk={chunk}")
+    lps, lss = [], []
+    for c0 in range(0, N, chunk):
+        lp, ls = run_ex(h[c0:c0 + chunk], inp["weight"], t[c0:c0 + chunk], inp["bias"])
+        lps.append(lp)
+        lss.append(ls)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(lps), full_lp), f"chunk {chunk} changed logp bits"
+    assert torch.equal(torch.cat(lss), full_ls), f"chunk {chunk} changed lse bits"
+
+
+def test_run_to_run():
+    inp, full_lp, full_ls = sweep_inputs()
+    say("sweep run-to-run x3")
+    for _ in range(3):
+        lp, ls = run_inputs(inp)
+        torch.cuda.synchronize()
+        assert torch.equal(lp, full_lp) and torch.equal(ls, full_ls)
+
+
+def test_side_stream():
+    inp, full_lp, full_ls = sweep_inputs()
+    s = torch.cuda.Stream()
+    say("sweep on a side stream")
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        lp, ls = run_inputs(inp, stream=s)
+    s.synchronize()
+    assert torch.equal(lp, full_lp) and torch.equal(ls, full_ls)
+
+
+def test_row_position():
+    """One row placed at every slot of a 256-row block (and at slot 0 of the
+    next block, N = 257) gives the bits it has inside the full batch."""
+    inp, full_lp, full_ls = sweep_inputs()
+    h, t = flat(inp)
+    for r in (0, 1234, 4095):
+        hh = h[r:r + 1].expand(257, -1).contiguous()
+        tt = t[r:r + 1].expand(257).contiguous()
+        say(f"row position r={r}")
+        lp, ls = run_ex(hh, inp["weight"], tt, inp["bias"])
+        torch.cuda.synchronize()
+        assert torch.equal(lp, full_lp[r].expand(257)), f"row {r}: logp depends on slot"
+        assert torch.equal(ls, full_ls[r].expand(257)), f"row {r}: lse depends on slot"
+
+
+def test_neighbours():
+    """Replacing every other row by fresh random rows leaves the kept rows' bits."""
+    inp, full_lp, full_ls = sweep_inputs()
+    h, t = flat(inp)
+    g = torch.Generator(device=DEV).manual_seed(1234)
+    h2 = torch.randn(h.shape, generator=g, device=DEV).to(torch.bfloat16)
+    t2 = torch.randint(0, inp["weight"].shape[0], t.shape, generator=g, device=DEV)
+    keep = torch.arange(0, h.shape[0], 3, device=DEV)
+    h2[keep] = h[keep]
+    t2[keep] = t[keep]
+    say("neighbours replaced")
+    lp, ls = run_ex(h2, inp["weight"], t2, inp["bias"])
+    torch.cuda.synchronize()
+    assert torch.equal(lp[keep], full_lp[keep]) and torch.equal(ls[keep], full_ls[keep])
+
+
+def test_layouts():
+    """[8, 512, H] input vs its [4096, H] reshape vs a strided view made
+    contiguous by the wrapper: identical bits (headline workload)."""
+    inp = synth.make_inputs("headline", device=DEV)
+    h3, w, t2 = inp["hidden"], inp["weight"], inp["target"]
+    say("layouts headline")
+    lp3, ls3 = ila.forward(h3, w, t2, check_targets=False)
+    lp2, ls2 = run_ex(h3.reshape(-1, h3.shape[-1]), w, t2.reshape(-1))
+    wide = torch.zeros(h3.shape[0], h3.shape[1], h3.shape[2] + 64, dtype=torch.bfloat16,
+                       device=DEV)
+    wide[..., 32:32 + h3.shape[2]] = h3
+    view = wide[..., 32:32 + h3.shape[2]]
+    assert not view.is_contiguous()
+    lpv, lsv = ila.forward(view, w, t2.expand(8, 512), check_targets=False)
+    # a zero-stride (expanded) target is accepted
+    t_exp = t2[:, :1].expand(8, 512)
+    lpe, _ = ila.forward(h3, w, t_exp, check_targets=False)
+    lpe2, _ = run_ex(h3.reshape(-1, h3.shape[-1]), w, t_exp.reshape(-1).contiguous())
+    torch.cuda.synchronize()
+    assert lp3.shape == (8, 512)
+    assert torch.equal(lp3.reshape(-1), lp2) and torch.equal(ls3.reshape(-1), ls2)
+    assert torch.equal(lpv, lp3) and torch.equal(lsv, ls3)
+    assert torch.equal(lpe.reshape(-1), lpe2)

@@ -1,0 +1,250 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Full comparison where the oracle takes seconds (the tiny and medium
+workloads and ragged shapes spanning several tiles, splits and row blocks);
+seeded row samples at the three large workloads, run in the same launch
+configuration the benchmark times, plus properties that hold at any size.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import invariant_linear_log_amd as ila
+import oracle
+import synth
+from gpu_common import (DEV, TOL, assert_parity, flat, oracle_rows, peaky_with_argmax_targets,
+                        run_ex, run_inputs, sample_rows, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def test_tiny_full():
+    inp = synth.make_inputs("tiny", device=DEV)
+    say("tiny N=8 H=64 V=1000")
+    logp, lse = run_inputs(inp)
+    torch.cuda.synchronize()
+    ref_lp, ref_ls = oracle_rows(inp)
+    assert_parity(logp, lse, ref_lp, ref_ls, what="tiny")
+
+
+def test_medium_full():
+    inp = synth.make_inputs("medium", device=DEV)
+    say("medium N=512 H=1024 V=32000 fp32 bias")
+    logp, lse = run_inputs(inp)
+    torch.cuda.synchronize()
+    ref_lp, ref_ls = oracle_rows(inp)
+    assert_parity(logp, lse, ref_lp, ref_ls, what="medium")
+
+
+RAGGED = [
+    # N, H, V, bias, seed: ragged rows / K / vocabulary tail / split counts
+    (300, 200, 2000, None, 101),     # 2 row blocks (256 + 44); H % 32 = 8; 208-col tail; 8 splits
+    (37, 256, 70000, "f32", 102),    # 274 tiles -> 5 per split -> 55 splits (last has 4)
+    (513, 64, 257, "bf16", 103),     # 3 row blocks; last tile has 1 column
+    (5, 8, 1, None, 104),            # V = 1 (logp = 0); H = 8 (one 8-wide K chunk)
+    (1, 4096, 16385, "bf16", 105),   # N = 1; 65 tiles -> 33 splits, last split one column
+    (64, 512, 16384, None, 106),     # exactly 64 splits of one tile
+    (260, 136, 5003, "f32", 107),    # H = 136 (17 chunks), tail of 139 columns
+]
+
+
+@pytest.mark.parametrize("N,H,V,bias,seed", RAGGED)
+def test_ragged_full(N, H, V, bias, seed):
+    inp = synth.make_custom(N, H, V, seed=seed, bias=bias, device=DEV)
+    say(f"ragged N={N} H={H} V={V} bias={bias}")
+    logp, lse = run_inputs(inp)
+    torch.cuda.synchronize()
+    ref_lp, ref_ls = oracle_rows(inp)
+    assert_parity(logp, lse, ref_lp, ref_ls, what=f"ragged N={N} H={H} V={V}")
+    if V == 1:
+        assert torch.all(logp == 0)
+
+
+@pytest.mark.parametrize("name,k", [("headline", 512), ("sweep", 256)])
+def test_large_sampled(name, k):
+    inp = synth.make_inputs(name, device=DEV)
+    wl = inp["workload"]
+    say(f"{name} N={wl.N} H={wl.H} V={wl.V}")
+    logp, lse = run_inputs(inp)
+    torch.cuda.synchronize()
+    assert bool(torch.all(logp <= 0)), "logp > 0"
+    assert bool(torch.all(torch.isfinite(lse)))
+    rows = sample_rows(wl.N, k, seed=wl.seed)
+    ref_lp, ref_ls = oracle_rows(inp, rows=rows)
+    assert_parity(logp, lse, ref_lp, ref_ls, rows=rows, what=name)
+
+
+def test_peaky_sampled():
+    inp, arg_rows = peaky_with_argmax_targets()
+    wl = inp["workload"]
+    say(f"peaky N={wl.N} H={wl.H} V={wl.V}")
+    logp, lse = run_inputs(inp)
+    torch.cuda.synchronize()
+    assert bool(torch.all(logp <= 0)), "logp > 0"
+    assert bool(torch.all(torch.isfinite(lse)))
+    lnv = math.log(wl.V)
+    assert bool(torch.all(logp[arg_rows] >= -lnv - TOL)), "argmax row below -ln V"
+    g = np.random.default_rng(44)
+    arg = arg_rows.cpu().numpy()
+    other = np.setdiff1d(np.arange(wl.N), arg)
+    rows = np.unique(np.concatenate([g.choice(arg, 256, replace=False),
+                                     g.choice(other, 254, replace=False), [0, wl.N - 1]]))
+    ref_lp, ref_ls = oracle_rows(inp, rows=rows)
+    assert_parity(logp, lse, ref_lp, ref_ls, rows=rows, what="peaky")
+
+
+@pytest.mark.parametrize("V", [1000, 32000, 128256, 152064])
+def test_zero_weight_closed_form(V):
+    """W = 0, no bias: logp = -ln V and lse = ln V (every logit is exactly 0,
+    the sum is exactly V < 2^24), and lse has the same bits on every row."""
+    N, H = 300, 64
+    g = torch.Generator().manual_seed(V)
+    h = torch.randn(N, H, generator=g).to(torch.bfloat16).to(DEV)
+    w = torch.zeros(V, H, dtype=torch.bfloat16, device=DEV)
+    t = torch.randint(0, V, (N,), generator=g).to(DEV)
+    say(f"W=0 V={V}")
+    logp, lse = run_ex(h, w, t)
+    torch.cuda.synchronize()
+    lnv = math.log(V)
+    # the sum is exactly V; ln V comes from the hardware log2 (about 1 ulp)
+    # times ln 2 in fp32: allow 4 fp32 ulps of ln V
+    tol = 4 * float(np.spacing(np.float32(lnv)))
+    assert float((logp.double() + lnv).abs().max()) <= tol
+    assert float((lse.double() - lnv).abs().max()) <= tol
+    assert torch.equal(lse, lse[:1].expand(N)), "lse bits differ across rows"
+    assert torch.equal(logp, -lse), "logp != -lse with all logits zero"
+
+
+@pytest.mark.parametrize("V", [257, 259, 2 * 256 + 3, 16384 + 5])
+@pytest.mark.parametrize("bias_dtype", [torch.bfloat16, torch.float32])
+def test_bias_on_ragged_vocab_tail(V, bias_dtype):
+    """W = 0 and a unit-scale bias: every bias entry moves lse, and a target
+    in the last (partial) tile reads its own bias; checked against the oracle."""
+    N, H = 40, 64
+    g = torch.Generator().manual_seed(V)
+    h = torch.randn(N, H, generator=g).to(torch.bfloat16)
+    w = torch.zeros(V, H, dtype=torch.bfloat16)
+    b = torch.randn(V, generator=g).to(bias_dtype)
+    t = torch.randint(0, V, (N,), generator=g)
+    t[:8] = torch.arange(V - 8, V)
+    say(f"bias tail V={V} {bias_dtype}")
+    logp, lse = run_ex(h.to(DEV), w.to(DEV), t.to(DEV), b.to(DEV))
+    torch.cuda.synchronize()
+    ref_lp, ref_ls = oracle.linear_logp(h, w, t, b)
+    assert_parity(logp, lse, ref_lp, ref_ls, tol=1e-4, what=f"bias tail V={V}")
+
+
+@pytest.mark.parametrize("name", ["medium", "sweep"])
+def test_zero_weight_with_bias(name):
+    """W = 0 with the workload's bias: lse is LSE(bias) on every row (same
+    bits), logp = bias[t] - LSE(bias)."""
+    inp = synth.make_inputs(name, device=DEV, variant="w0")
+    say(f"W=0 + bias {name}")
+    logp, lse = run_inputs(inp)
+    torch.cuda.synchronize()
+    N = lse.shape[0]
+    assert torch.equal(lse, lse[:1].expand(N)), "lse bits differ across rows"
+    rows = sample_rows(N, 64, seed=9)
+    ref_lp, ref_ls = oracle_rows(inp, rows=rows)
+    assert_parity(logp, lse, ref_lp, ref_ls, rows=rows, what=f"w0+bias {name}")
+
+
+def test_bias_shift():
+    """Bias values on a 2^-10 grid with |b| < 8, so b + 1 is exact in fp32:
+    logp moves by <= tol, lse by 1 +- tol; both runs match the oracle."""
+    inp = synth.make_custom(300, 256, 3000, seed=77, device="cpu")
+    g = torch.Generator().manual_seed(78)
+    b = torch.round(torch.randn(3000, generator=g) * 0.1 * 1024) / 1024
+    h, w, t = inp["hidden"].to(DEV), inp["weight"].to(DEV), inp["target"].to(DEV)
+    say("bias shift")
+    lp1, ls1 = run_ex(h, w, t, b.to(DEV))
+    lp2, ls2 = run_ex(h, w, t, (b + 1.0).to(DEV))
+    torch.cuda.synchronize()
+    assert float((lp1 - lp2).abs().max()) <= TOL
+    assert float((ls2 - ls1 - 1.0).abs().max()) <= TOL
+    r1 = oracle.linear_logp(inp["hidden"], inp["weight"], inp["target"], b)
+    r2 = oracle.linear_logp(inp["hidden"], inp["weight"], inp["target"], b.double() + 1.0)
+    assert_parity(lp1, ls1, *r1, what="bias b")
+    assert_parity(lp2, ls2, *r2, what="bias b+1")
+
+
+def test_normalisation_and_row_position():
+    """Row 0 of the tiny workload repeated V = 1000 times (4 row blocks) with
+    targets 0..999: sum_v exp(logp_v) = 1 and lse has one bit pattern."""
+    inp = synth.make_inputs("tiny", device=DEV)
+    V = inp["weight"].shape[0]
+    h = inp["hidden"][:1].expand(V, -1).contiguous()
+    t = torch.arange(V, device=DEV)
+    say("normalisation N=1000 copies of one row")
+    logp, lse = run_ex(h, inp["weight"], t)
+    torch.cuda.synchronize()
+    total = math.fsum(math.exp(x) for x in logp.double().cpu().tolist())
+    assert abs(total - 1.0) <= 1e-4, total
+    assert torch.equal(lse, lse[:1].expand(V))
+    assert bool(torch.all(logp <= 0))
+
+
+def test_out_of_range_targets_give_nan():
+    inp = synth.make_custom(40, 64, 700, seed=88, device=DEV)
+    h, w, t = inp["hidden"], inp["weight"], inp["target"]
+    bad = t.clone()
+    bad[3], bad[17], bad[39] = -1, 700, 10 ** 12
+    say("out-of-range targets")
+    lp_ok, ls_ok = run_ex(h, w, t)
+    lp_bad, ls_bad = run_ex(h, w, bad)
+    torch.cuda.synchronize()
+    nan = torch.isnan(lp_bad)
+    assert nan.tolist() == [i in (3, 17, 39) for i in range(40)]
+    assert torch.equal(lp_bad[~nan], lp_ok[~nan])
+    assert torch.equal(ls_bad, ls_ok)
+    with pytest.raises(ValueError, match="outside"):
+        ila.forward(h, w, bad)
+
+
+def test_empty_batch():
+    w = torch.zeros(100, 64, dtype=torch.bfloat16, device=DEV)
+    h = torch.zeros(0, 64, dtype=torch.bfloat16, device=DEV)
+    t = torch.zeros(0, dtype=torch.int64, device=DEV)
+    lp, ls = ila.forward(h, w, t)
+    assert lp.shape == (0,) and ls.shape == (0,)
+    lp, ls = ila.forward(h.reshape(0, 0, 64), w, t.reshape(0, 0))
+    assert lp.shape == (0, 0)
+
+
+def test_library_workspace_entry_point_matches():
+    """bilogp_forward (stream-ordered internal workspace, fp32 bias) gives the
+    same bits as bilogp_forward_ex with a caller workspace."""
+    inp = synth.make_inputs("medium", device=DEV)
+    h, t = flat(inp)
+    N = h.shape[0]
+    lp1, ls1 = run_inputs(inp)
+    lp2 = torch.empty(N, device=DEV)
+    ls2 = torch.empty(N, device=DEV)
+    say("bilogp_forward vs bilogp_forward_ex")
+    ila.bilogp_forward(h, inp["weight"], t, inp["bias"], lp2, ls2)
+    torch.cuda.synchronize()
+    assert torch.equal(lp1, lp2) and torch.equal(ls1, ls2)
+
+
+def test_wrong_device_architecture_fields():
+    """The library accepts this device (gfx950) and reports no error."""
+    assert torch.cuda.get_device_properties(0).gcnArchName.startswith("gfx950")
+    inp = synth.make_inputs("tiny", device=DEV)
+    run_inputs(inp)
+    torch.cuda.synchronize()
+    assert ila.bilogp_last_error() == ""
+
+
+def test_host_pointer_rejected():
+    """A host pointer where device memory is required fails closed."""
+    inp = synth.make_inputs("tiny", device=DEV)
+    h, t = flat(inp)
+    lp = torch.empty(8, device=DEV)
+    ls = torch.empty(8, device=DEV)
+    ws = ila.workspace_for(8, 1000, DEV)
+    with pytest.raises(ila.BilogpError) as e:
+        ila.bilogp_forward_ex(h, inp["weight"].cpu(), t, None, lp, ls, ws)
+    assert e.value.status == ila.BILOGP_E_UNSUPPORTED
