@@ -43,7 +43,22 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of the workload the CPU oracle is timed on")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 3 device copies of MIB MiB (a plain copy kernel of known "
+                         "size, to scale the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+def calibrate_copy(mib):
+    import torch
+    n = mib * (1 << 20)
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}), flush=True)
 
 
 def algorithmic_bytes(N, H, V, S, bias_bytes):
@@ -78,6 +93,9 @@ def cpu_baseline(inp, rows_n, seed=7):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); rows are independent, "
               "so N GPUs would each run this same single-GPU step on their own rows.",
