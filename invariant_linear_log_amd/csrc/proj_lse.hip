@@ -38,6 +38,20 @@
 // row block) and K chunks past H read as zero through the buffer
 // descriptors' range check.
 //
+// Instruction schedule of a stage (four 16-wide K steps u = 0..3): the
+// operand fragments of step u + 1 are read from LDS while the MFMAs of step
+// u run (two fragment sets in registers), so LDS latency - which grows while
+// the direct loads are writing LDS - stays off the MFMA path.  The stage's
+// barrier sits before step 3: once every wave has read step 3's operands
+// and its loads of the next stage have landed, the buffer is released, the
+// loads of stage g + 2 are issued into it and the next stage's step-0
+// operands are read, all under the MFMAs of step 3.
+//
+// Bias.  Each logit's accumulation starts from its bias value (fp32, from
+// the padded copy the host library prepares), loaded straight into the
+// accumulator registers when a vocabulary tile starts; the K products are
+// then added in ascending order.  Without bias the accumulators start at 0.
+//
 // LDS layout.  Each 256 x 64 slice is 256 rows of eight 16-byte chunks,
 // chunk c of row r stored at position c ^ f(r), f(r) = (r >> 1) & 7.
 // gfx950 serves a 16-byte-per-lane LDS read in four passes of 16 lanes over
@@ -67,7 +81,7 @@ constexpr int kBK = 64;                            // K per stage
 constexpr int kChunks = kBK / 8;                   // 16-byte chunks per slice row
 constexpr int kLdsRowBytes = kBK * 2;              // 128 B per slice row
 constexpr int kTileBytes = kVtileCols * kLdsRowBytes;         // 32 KB: one operand slice
-constexpr int kSlotBytes = 2 * kTileBytes + kVtileCols * 4;   // W, hidden, bias
+constexpr int kSlotBytes = 2 * kTileBytes;                    // W, hidden
 constexpr int kLoadsPerOperand = kTileBytes / (kThreads * 16);  // 4 per wave and stage
 constexpr int kRowBlockGroup = 4;                  // row blocks per tile-order group
 constexpr uint32_t kOutOfRange = 0x7ffffff0u;      // any offset past num_records
@@ -105,7 +119,7 @@ __global__ __launch_bounds__(kThreads, 1) void proj_lse_kernel(const ProjParams 
   // Two LDS buffers, each its own variable, so the compiler can tell a read
   // of one from a direct-to-LDS load into the other and does not drain the
   // load pipeline before every read.  Buffer layout: W slice (32 KB), hidden
-  // slice (32 KB), bias of the tile (1 KB, used in buffer 1 only).
+  // slice (32 KB).
   __shared__ __attribute__((aligned(1024))) uint8_t slot0[kSlotBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t slot1[kSlotBytes];
   __shared__ float2 red[kBlockRows];
@@ -212,68 +226,111 @@ __global__ __launch_bounds__(kThreads, 1) void proj_lse_kernel(const ProjParams 
           rsrc_h, (lds_void*)(st + kTileBytes + (wave * kLoadsPerOperand + j) * 1024), 16,
           voff, 0, 0, 0);
     }
-    if constexpr (decltype(sc)::value == 1) {
-      // the tile's bias rides with its last stage (always buffer 1), which is
-      // still intact when the tile's epilogue runs; the bias copy is fp32 and
-      // padded to whole tiles, so all 64 lanes' 16-byte chunks are in range
-      if (kt == KT - 1 && p.bias_kind != kBiasNone && wave == 0) {
-        const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)((const float*)p.bias + vbase), (short)0, kVtileCols * 4, kRsrcWord3);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_b, (lds_void*)(st + 2 * kTileBytes), 16,
-                                                 (uint32_t)lane * 16u, 0, 0, 0);
-      }
-    }
   };
 
   floatx16 acc[4][2];
-#pragma unroll
-  for (int vi = 0; vi < 4; ++vi)
-#pragma unroll
-    for (int ti = 0; ti < 2; ++ti) acc[vi][ti] = floatx16{};
 
-  // MFMAs of the stage held in buffer SC: four 16-wide K steps, ascending.
-  auto compute = [&](auto sc) {
-    const uint8_t* st = slot_ptr(sc);
-#pragma unroll
-    for (int uu = 0; uu < 4; ++uu) {
-      bf16x8 a[4], b[2];
-#pragma unroll
-      for (int vi = 0; vi < 4; ++vi)
-        a[vi] = *(const bf16x8*)(st + a_off[uu] + vi * 32 * kLdsRowBytes);
-#pragma unroll
-      for (int ti = 0; ti < 2; ++ti)
-        b[ti] = *(const bf16x8*)(st + b_off[uu] + ti * 32 * kLdsRowBytes);
+  // Start the accumulators of vocabulary tile v: the tile's bias values, or 0.
+  // acc[vi][ti][r] belongs to vocabulary row wv*128 + vi*32 + 8*(r/4) +
+  // 4*half + (r%4) of the tile (for both token columns ti).
+  auto init_acc = [&](int v) {
+    if (p.bias_kind != kBiasNone && v < nvt) {
+      const float* bt = (const float*)p.bias + (vt_begin + v) * kVtileCols + wv * 128 + 4 * half;
 #pragma unroll
       for (int vi = 0; vi < 4; ++vi)
 #pragma unroll
-        for (int ti = 0; ti < 2; ++ti)
-          acc[vi][ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[vi], b[ti], acc[vi][ti], 0, 0, 0);
+        for (int q = 0; q < 4; ++q) {
+          const floatx4 bb = *(const floatx4*)(bt + vi * 32 + 8 * q);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[vi][0][4 * q + e] = bb[e];
+            acc[vi][1][4 * q + e] = bb[e];
+          }
+        }
+    } else {
+#pragma unroll
+      for (int vi = 0; vi < 4; ++vi)
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti) acc[vi][ti] = floatx16{};
     }
   };
 
-  // Wait for this wave's loads of the stage about to be computed (the only
-  // ones in flight), then barrier: afterwards every wave's data for it is in
-  // LDS and nobody still reads the other buffer.  The barrier is a bare
-  // s_barrier (the compiler-level memory clobber keeps LDS accesses on their
-  // side of it); a C++ workgroup fence would also wait for unrelated stores.
+  // Operand fragments of K step uu of the stage in buffer st, read in the
+  // order the MFMAs (vi, ti) = (0,0), (0,1), (1,0), ... first need them.
+  auto read_frags = [&](const uint8_t* st, int uu, bf16x8 (&a)[4], bf16x8 (&b)[2]) {
+    b[0] = *(const bf16x8*)(st + b_off[uu]);
+    a[0] = *(const bf16x8*)(st + a_off[uu]);
+    b[1] = *(const bf16x8*)(st + b_off[uu] + 32 * kLdsRowBytes);
+#pragma unroll
+    for (int vi = 1; vi < 4; ++vi)
+      a[vi] = *(const bf16x8*)(st + a_off[uu] + vi * 32 * kLdsRowBytes);
+  };
+  auto mfmas = [&](const bf16x8 (&a)[4], const bf16x8 (&b)[2]) {
+#pragma unroll
+    for (int vi = 0; vi < 4; ++vi)
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+        acc[vi][ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[vi], b[ti], acc[vi][ti], 0, 0, 0);
+  };
+  // Keep the scheduler from sinking the next step's LDS reads onto their
+  // uses: alternate MFMA and LDS read, one each, then the remaining MFMAs.
+  auto pin_reads = [&]() {
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  };
+
+  // Wait for this wave's loads of the next stage (the only ones in flight)
+  // and for its LDS reads, then barrier: afterwards every wave's next-stage
+  // data is in LDS and nobody reads the current buffer any more.  The barrier
+  // is a bare s_barrier (the compiler-level memory clobber keeps LDS accesses
+  // on their side of it); a C++ workgroup fence would also wait for stores.
   auto sync_stage = [&]() {
     wait_vmcnt<0>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+
+  bf16x8 fa0[4], fb0[2], fa1[4], fb1[2];
+
+  // Stage g, computed from buffer SC; buffer SN holds stage g + 1.  On entry
+  // fa0/fb0 hold step 0 of stage g; on exit they hold step 0 of stage g + 1.
+  auto stage = [&](int g, auto sc, auto sn) {
+    const uint8_t* st = slot_ptr(sc);
+    read_frags(st, 1, fa1, fb1);
+    mfmas(fa0, fb0);
+    pin_reads();
+    read_frags(st, 2, fa0, fb0);
+    mfmas(fa1, fb1);
+    pin_reads();
+    read_frags(st, 3, fa1, fb1);
+    mfmas(fa0, fb0);
+    pin_reads();
+    sync_stage();
+    issue(g + 2, sc);
+    if (g + 1 < G) read_frags(slot_ptr(sn), 0, fa0, fb0);
+    mfmas(fa1, fb1);
   };
 
   float m_run[2] = {-INFINITY, -INFINITY};
   float s_run[2] = {0.f, 0.f};
 
   issue(0, Slot<0>{});
+  issue(1, Slot<1>{});
+  init_acc(0);
+  if (G > 1)
+    wait_vmcnt<2 * kLoadsPerOperand>();           // stage 0 landed, stage 1 may be in flight
+  else
+    wait_vmcnt<0>();
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  read_frags(slot0, 0, fa0, fb0);
 
   // G is even: stage g lives in buffer 0, stage g + 1 in buffer 1.
   for (int g = 0; g < G; g += 2) {
-    sync_stage();
-    issue(g + 1, Slot<1>{});
-    compute(Slot<0>{});
-    sync_stage();
-    issue(g + 2, Slot<0>{});
-    compute(Slot<1>{});
+    stage(g, Slot<0>{}, Slot<1>{});
+    stage(g + 1, Slot<1>{}, Slot<0>{});
 
     const int v = g / KT;
     if (g + 2 != (v + 1) * KT) continue;
@@ -283,21 +340,6 @@ __global__ __launch_bounds__(kThreads, 1) void proj_lse_kernel(const ProjParams 
     // vocabulary row wv*128 + vi*32 + 8*(r/4) + 4*half + (r%4) of the tile.
     const int vbase = (vt_begin + v) * kVtileCols;
     const int vw = vbase + wv * 128;               // first column of this wave
-    if (p.bias_kind != kBiasNone) {
-      const uint8_t* braw = slot1 + 2 * kTileBytes;
-#pragma unroll
-      for (int vi = 0; vi < 4; ++vi)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c0 = wv * 128 + vi * 32 + 8 * q + 4 * half;
-          const floatx4 bb = *(const floatx4*)(braw + c0 * 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[vi][0][4 * q + e] += bb[e];
-            acc[vi][1][4 * q + e] += bb[e];
-          }
-        }
-    }
     if (vbase + kVtileCols > p.V) {                // vocabulary tail: mask columns >= V
 #pragma unroll
       for (int vi = 0; vi < 4; ++vi)
@@ -346,10 +388,7 @@ __global__ __launch_bounds__(kThreads, 1) void proj_lse_kernel(const ProjParams 
       s_run[ti] = s_run[ti] * exp2_hw((m_run[ti] - mu) * kLog2e) + tile_sum;
       m_run[ti] = m_new;
     }
-#pragma unroll
-    for (int vi = 0; vi < 4; ++vi)
-#pragma unroll
-      for (int ti = 0; ti < 2; ++ti) acc[vi][ti] = floatx16{};
+    init_acc(v + 1);
   }
 
   // ---- split done: merge lane halves, then the two vocabulary-half waves ----
