@@ -33,6 +33,14 @@ METRIC = "tokens/s + TFLOP/s (MFMA %peak), linear-logp N=4096 H=4096 V=128256 bf
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0
 
+# HBM-side bytes per launch of proj_lse_kernel on the headline workload, from two
+# rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE), each scaled by what the same counter
+# reads for a plain 1 GiB device copy (x2.000 and x1.000).  Keyed by the sha256 prefix
+# of the kernel source the counters were taken on: any other source reports null.
+MEASURED_TRAFFIC = {
+    ("headline", "b18ab2f4abc37e34"): {"fetch_bytes": 6727413229, "write_bytes": 45400768},
+}
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -65,6 +73,15 @@ def algorithmic_bytes(N, H, V, S, bias_bytes):
     """Bytes the forward must move at least once: W, hidden, targets, bias,
     the partials written and read back, target logits, and the outputs."""
     return (V * H * 2 + N * H * 2 + N * 8 + bias_bytes + 2 * N * S * 8 + 2 * N * 4 + 2 * N * 4)
+
+
+def measured_traffic(workload):
+    import hashlib
+    src = os.path.join(ROOT, "invariant_linear_log_amd", "csrc", "proj_lse.hip")
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    rec = MEASURED_TRAFFIC.get((workload, sha))
+    return None if rec is None else rec["fetch_bytes"] + rec["write_bytes"]
 
 
 def cpu_baseline(inp, rows_n, seed=7):
@@ -180,7 +197,8 @@ def main():
                      "frac": tflops_proj / PEAK_BF16_TFLOPS,
                      "algorithmic_flops": flops,
                      "algorithmic_bytes": algorithmic_bytes(N, H, V, S, bias_bytes),
-                     "traffic": None},
+                     "traffic": measured_traffic(wl.name),
+                     "traffic_unit": "bytes per launch"},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows)

@@ -25,8 +25,8 @@ operator".
 Readings where the page is silent (each is repeated in the design notes):
   * logits are not rounded to a narrow type before the log-sum-exp; the oracle
     keeps them in float64;
-  * the optional bias has shape [V] and is added once, after the whole
-    contraction;
+  * the optional bias has shape [V] and is added once to each logit (in
+    float64 the order of that one addition is immaterial);
   * "log" is the natural logarithm;
   * a target must lie in [0, V); there is no ignore index.
 
