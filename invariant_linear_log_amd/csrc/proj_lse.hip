@@ -43,9 +43,14 @@
 // u run (two fragment sets in registers), so LDS latency - which grows while
 // the direct loads are writing LDS - stays off the MFMA path.  The stage's
 // barrier sits before step 3: once every wave has read step 3's operands
-// and its loads of the next stage have landed, the buffer is released, the
-// loads of stage g + 2 are issued into it and the next stage's step-0
-// operands are read, all under the MFMAs of step 3.
+// and its loads of the next stage have landed, the buffer is released and
+// refilled with stage g + 2 - the W slice under the MFMAs of step 3, the
+// hidden slice under those of step 0 of stage g + 1.  Each of these steps
+// is emitted in a fixed order (MFMA, LDS read, and a direct load after every
+// second MFMA): the texture-address unit takes one 1 KB load about every 16
+// cycles, so a wave that issued its loads in one burst would sit at the load
+// instruction, with its MFMAs queued behind it, until the unit drained.
+// Interleaved, the loads drain while the matrix cores work.
 //
 // Bias.  Each logit's accumulation starts from its bias value (fp32, from
 // the padded copy the host library prepares), loaded straight into the
@@ -115,7 +120,10 @@ __device__ __forceinline__ void merge_state(float m_lo, float s_lo, float m_hi, 
 template <int I>
 using Slot = std::integral_constant<int, I>;
 
-__global__ __launch_bounds__(kThreads, 1) void proj_lse_kernel(const ProjParams p) {
+// The kernel body, instantiated once with bias and once without (two plain
+// kernels below), so the bias-free path carries no bias code.
+template <bool kHasBias>
+__device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
   // Two LDS buffers, each its own variable, so the compiler can tell a read
   // of one from a direct-to-LDS load into the other and does not drain the
   // load pipeline before every read.  Buffer layout: W slice (32 KB), hidden
@@ -131,7 +139,7 @@ __global__ __launch_bounds__(kThreads, 1) void proj_lse_kernel(const ProjParams 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wv = wave & 1;
   const int wt = wave >> 1;
   const int half = lane >> 5;
@@ -199,33 +207,50 @@ __global__ __launch_bounds__(kThreads, 1) void proj_lse_kernel(const ProjParams 
     tgt[ti] = (j < rows_here) ? p.target[m0 + j] : (int64_t)-1;
   }
 
-  // Issue the direct-to-LDS loads of stage g into buffer SC.
-  auto issue = [&](int g, auto sc) {
-    if (g >= G) return;
+  // Direct-to-LDS loads of stage g into buffer SC, one instruction at a
+  // time: load j (0..3) of the W slice or of the hidden slice.  A stage past
+  // the end (g >= G) reads nothing (empty range) and writes zeros into a
+  // buffer that is no longer read; no branch, so the loads can sit between
+  // MFMAs.
+  struct LoadCtx {
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint8_t* dst;
+    uint32_t k2;      // byte offset of the stage's K slice
+    int kend;         // H, or 0 for a stage past the end
+  };
+  auto ctx_w = [&](int g, auto sc) {
     const int v = g / KT;
     const int kt = g - v * KT;
-    const int k0 = kt * kBK;
     const int vbase = (vt_begin + v) * kVtileCols;
-    const int vrows = min(kVtileCols, p.V - vbase);
-    uint8_t* st = slot_ptr(sc);
-    const __amdgpu_buffer_rsrc_t rsrc_w = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const uint16_t*)p.weight + (int64_t)vbase * H), (short)0, vrows * H * 2,
-        kRsrcWord3);
-#pragma unroll
-    for (int j = 0; j < kLoadsPerOperand; ++j) {
-      const bool ok = k0 + kchunk[j] < H;
-      const uint32_t voff = ok ? voff_base[j] + (uint32_t)k0 * 2u : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc_w, (lds_void*)(st + (wave * kLoadsPerOperand + j) * 1024), 16, voff, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < kLoadsPerOperand; ++j) {
-      const bool ok = k0 + kchunk[j] < H;
-      const uint32_t voff = ok ? voff_base[j] + (uint32_t)k0 * 2u : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc_h, (lds_void*)(st + kTileBytes + (wave * kLoadsPerOperand + j) * 1024), 16,
-          voff, 0, 0, 0);
-    }
+    const int vrows = (g < G) ? min(kVtileCols, p.V - vbase) : 0;
+    int dst = wave * kLoadsPerOperand * 1024;
+    asm volatile("" : "+s"(dst));     // recomputed per stage: LDS addresses stay out of SGPRs
+    LoadCtx c;
+    c.rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint16_t*)p.weight + (int64_t)(g < G ? vbase : 0) * H), (short)0,
+        vrows * H * 2, kRsrcWord3);
+    c.dst = slot_ptr(sc) + dst;
+    c.k2 = (uint32_t)(kt * kBK) * 2u;
+    c.kend = H;
+    return c;
+  };
+  auto ctx_h = [&](int g, auto sc) {
+    const int v = g / KT;
+    const int kt = g - v * KT;
+    int dst = kTileBytes + wave * kLoadsPerOperand * 1024;
+    asm volatile("" : "+s"(dst));
+    LoadCtx c;
+    c.rsrc = rsrc_h;
+    c.dst = slot_ptr(sc) + dst;
+    c.k2 = (uint32_t)(kt * kBK) * 2u;
+    c.kend = (g < G) ? H : 0;
+    return c;
+  };
+  auto load_one = [&](const LoadCtx& c, int j) {
+    const bool ok = (int)(c.k2 / 2u) + kchunk[j] < c.kend;
+    const uint32_t voff = ok ? voff_base[j] + c.k2 : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsrc, (lds_void*)(c.dst + j * 1024), 16, voff, 0,
+                                             0, 0);
   };
 
   floatx16 acc[4][2];
@@ -234,7 +259,7 @@ __global__ __launch_bounds__(kThreads, 1) void proj_lse_kernel(const ProjParams 
   // acc[vi][ti][r] belongs to vocabulary row wv*128 + vi*32 + 8*(r/4) +
   // 4*half + (r%4) of the tile (for both token columns ti).
   auto init_acc = [&](int v) {
-    if (p.bias_kind != kBiasNone && v < nvt) {
+    if (kHasBias && v < nvt) {
       const float* bt = (const float*)p.bias + (vt_begin + v) * kVtileCols + wv * 128 + 4 * half;
 #pragma unroll
       for (int vi = 0; vi < 4; ++vi)
@@ -255,8 +280,31 @@ __global__ __launch_bounds__(kThreads, 1) void proj_lse_kernel(const ProjParams 
     }
   };
 
-  // Operand fragments of K step uu of the stage in buffer st, read in the
-  // order the MFMAs (vi, ti) = (0,0), (0,1), (1,0), ... first need them.
+  // One K step in a fixed instruction order: MFMA i (tile (i/2, i%2)) is
+  // followed by LDS read i of the next step's fragments (i < 6) and, when a
+  // load context is given, by direct load i/2 after every odd MFMA.  The
+  // fences keep the compiler from regrouping: reads must not bunch up behind
+  // their uses, and loads issued in a burst would stall the wave (the
+  // texture-address unit takes one 1 KB load about every 16 cycles) and with
+  // it the MFMAs behind them.
+  auto step = [&](const bf16x8 (&a)[4], const bf16x8 (&b)[2], const uint8_t* nst, int nuu,
+                  bf16x8 (&na)[4], bf16x8 (&nb)[2], const LoadCtx& lc, auto with_loads) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int vi = i >> 1, ti = i & 1;
+      acc[vi][ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[vi], b[ti], acc[vi][ti], 0, 0, 0);
+      // next-step fragments in the order the MFMAs need them: b0 a0 b1 a1 a2 a3
+      if (i == 0) nb[0] = *(const bf16x8*)(nst + b_off[nuu]);
+      if (i == 1) na[0] = *(const bf16x8*)(nst + a_off[nuu]);
+      if (i == 2) nb[1] = *(const bf16x8*)(nst + b_off[nuu] + 32 * kLdsRowBytes);
+      if (i >= 3 && i < 6)
+        na[i - 2] = *(const bf16x8*)(nst + a_off[nuu] + (i - 2) * 32 * kLdsRowBytes);
+      if constexpr (decltype(with_loads)::value) {
+        if (i & 1) load_one(lc, i >> 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   auto read_frags = [&](const uint8_t* st, int uu, bf16x8 (&a)[4], bf16x8 (&b)[2]) {
     b[0] = *(const bf16x8*)(st + b_off[uu]);
     a[0] = *(const bf16x8*)(st + a_off[uu]);
@@ -264,23 +312,6 @@ __global__ __launch_bounds__(kThreads, 1) void proj_lse_kernel(const ProjParams 
 #pragma unroll
     for (int vi = 1; vi < 4; ++vi)
       a[vi] = *(const bf16x8*)(st + a_off[uu] + vi * 32 * kLdsRowBytes);
-  };
-  auto mfmas = [&](const bf16x8 (&a)[4], const bf16x8 (&b)[2]) {
-#pragma unroll
-    for (int vi = 0; vi < 4; ++vi)
-#pragma unroll
-      for (int ti = 0; ti < 2; ++ti)
-        acc[vi][ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[vi], b[ti], acc[vi][ti], 0, 0, 0);
-  };
-  // Keep the scheduler from sinking the next step's LDS reads onto their
-  // uses: alternate MFMA and LDS read, one each, then the remaining MFMAs.
-  auto pin_reads = [&]() {
-#pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
   };
 
   // Wait for this wave's loads of the next stage (the only ones in flight)
@@ -299,31 +330,31 @@ __global__ __launch_bounds__(kThreads, 1) void proj_lse_kernel(const ProjParams 
   // fa0/fb0 hold step 0 of stage g; on exit they hold step 0 of stage g + 1.
   auto stage = [&](int g, auto sc, auto sn) {
     const uint8_t* st = slot_ptr(sc);
-    read_frags(st, 1, fa1, fb1);
-    mfmas(fa0, fb0);
-    pin_reads();
-    read_frags(st, 2, fa0, fb0);
-    mfmas(fa1, fb1);
-    pin_reads();
-    read_frags(st, 3, fa1, fb1);
-    mfmas(fa0, fb0);
-    pin_reads();
+    const LoadCtx lh = ctx_h(g + 1, sn);
+    step(fa0, fb0, st, 1, fa1, fb1, lh, std::true_type{});
+    step(fa1, fb1, st, 2, fa0, fb0, lh, std::false_type{});
+    step(fa0, fb0, st, 3, fa1, fb1, lh, std::false_type{});
     sync_stage();
-    issue(g + 2, sc);
-    if (g + 1 < G) read_frags(slot_ptr(sn), 0, fa0, fb0);
-    mfmas(fa1, fb1);
+    const LoadCtx lw = ctx_w(g + 2, sc);
+    step(fa1, fb1, slot_ptr(sn), 0, fa0, fb0, lw, std::true_type{});
   };
 
   float m_run[2] = {-INFINITY, -INFINITY};
   float s_run[2] = {0.f, 0.f};
 
-  issue(0, Slot<0>{});
-  issue(1, Slot<1>{});
+  // Prologue: stage 0 whole and the W slice of stage 1 (its hidden slice is
+  // issued in stage 0).
+  {
+    const LoadCtx w0 = ctx_w(0, Slot<0>{}), h0 = ctx_h(0, Slot<0>{}), w1 = ctx_w(1, Slot<1>{});
+#pragma unroll
+    for (int j = 0; j < kLoadsPerOperand; ++j) load_one(w0, j);
+#pragma unroll
+    for (int j = 0; j < kLoadsPerOperand; ++j) load_one(h0, j);
+#pragma unroll
+    for (int j = 0; j < kLoadsPerOperand; ++j) load_one(w1, j);
+  }
   init_acc(0);
-  if (G > 1)
-    wait_vmcnt<2 * kLoadsPerOperand>();           // stage 0 landed, stage 1 may be in flight
-  else
-    wait_vmcnt<0>();
+  wait_vmcnt<0>();
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   read_frags(slot0, 0, fa0, fb0);
 
@@ -391,6 +422,10 @@ __global__ __launch_bounds__(kThreads, 1) void proj_lse_kernel(const ProjParams 
     init_acc(v + 1);
   }
 
+  // The last stages issued loads past the end (into buffers nobody reads);
+  // let them land before the workgroup's LDS is released.
+  wait_vmcnt<0>();
+
   // ---- split done: merge lane halves, then the two vocabulary-half waves ----
   float mm[2], ss[2];
 #pragma unroll
@@ -417,6 +452,13 @@ __global__ __launch_bounds__(kThreads, 1) void proj_lse_kernel(const ProjParams 
       if (j < rows_here) p.part[(m0 + j) * p.S + split] = make_float2(m, s);
     }
   }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void proj_lse_kernel(const ProjParams p) {
+  proj_lse_body<false>(p);
+}
+__global__ __launch_bounds__(kThreads, 1) void proj_lse_bias_kernel(const ProjParams p) {
+  proj_lse_body<true>(p);
 }
 
 // Exact fp32 copy of the bias (bf16 widens exactly), zero-padded to whole
@@ -447,7 +489,10 @@ hipError_t launch_bias_f32(const void* bias, int32_t kind, int32_t V, float* out
 hipError_t launch_proj_lse(const ProjParams& p, hipStream_t stream) {
   const int64_t blocks = (int64_t)p.R * p.S;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(proj_lse_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  if (p.bias_kind != kBiasNone)
+    hipLaunchKernelGGL(proj_lse_bias_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(proj_lse_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
