@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-invariance-cost", action="store_true",
+                    help="skip timing the throughput split policy beside the invariant one")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of the workload the CPU oracle is timed on")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -82,6 +84,41 @@ def measured_traffic(workload):
         sha = hashlib.sha256(f.read()).hexdigest()[:16]
     rec = MEASURED_TRAFFIC.get((workload, sha))
     return None if rec is None else rec["fetch_bytes"] + rec["write_bytes"]
+
+
+def invariance_cost(h, t, w, b, steps=10, warmup=3):
+    """ms per full forward step under the invariant and the throughput split
+    policies, at the workload's N and at its first 512 rows (fewer row blocks:
+    the throughput policy then adds splits to fill the device)."""
+    import torch
+    import invariant_linear_log_amd as ila
+    dev = h.device
+    cu = ila.device_cu_count(dev)
+    stream = torch.cuda.Stream(device=dev)
+    res = {"cu_count": cu}
+    for n in (h.shape[0], 512):
+        hn, tn = h[:n].contiguous(), t[:n].contiguous()
+        V = w.shape[0]
+        logp = torch.empty(n, dtype=torch.float32, device=dev)
+        lse = torch.empty(n, dtype=torch.float32, device=dev)
+        for name, mode in (("invariant", ila.BILOGP_SPLITS_INVARIANT),
+                           ("throughput", ila.BILOGP_SPLITS_THROUGHPUT)):
+            ws = ila.workspace_for(n, V, dev, name, cu)
+
+            def run():
+                ila.bilogp_forward_mode(hn, w, tn, b, logp, lse, mode, cu, ws, stream=stream)
+            for _ in range(warmup):
+                run()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                run()
+            e1.record(stream)
+            e1.synchronize()
+            res[f"n{n}_{name}_ms"] = e0.elapsed_time(e1) / steps
+            res[f"n{n}_{name}_splits"] = ila.bilogp_num_vocab_splits_mode(n, V, mode, cu)
+    return res
 
 
 def cpu_baseline(inp, rows_n, seed=7):
@@ -200,6 +237,8 @@ def main():
                      "traffic": measured_traffic(wl.name),
                      "traffic_unit": "bytes per launch"},
     }
+    if not args.no_invariance_cost:
+        out["invariance_cost"] = invariance_cost(h, t, w, b)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows)
     print(json.dumps(out), flush=True)

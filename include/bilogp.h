@@ -92,6 +92,42 @@ int bilogp_num_vocab_splits(int64_t V);
  * each 256-byte aligned.  0 for N == 0; (size_t)-1 for invalid N or V. */
 size_t bilogp_workspace_bytes(int64_t N, int64_t V);
 
+/* Split policies (RL-Kernel PR #337, description, "Why this happens" and its
+ * flowchart: the operator the page starts from has a throughput scheduler
+ * that picks the vocabulary split from N, V and the GPU's SM count, so one
+ * token row can be reduced as [A][B][C][D] in one batch and [A B][C D] in
+ * another; the pull request adds the V-only policy).
+ *
+ *   BILOGP_SPLITS_INVARIANT   the contract above: splits from V only.  Every
+ *                             entry point without a mode argument uses it.
+ *   BILOGP_SPLITS_THROUGHPUT  splits from N, V and a compute-unit count, for
+ *                             measuring what invariance costs.  The page gives
+ *                             no formula; with T tiles and R = ceil(N / 256)
+ *                             row blocks: want = min(max(ceil(cu_count / R), 1),
+ *                             T, BILOGP_MAX_THROUGHPUT_SPLITS), per_split =
+ *                             ceil(T / want), S = ceil(T / per_split) - enough
+ *                             splits that R x S approaches cu_count.  A row's
+ *                             bits then depend on N and cu_count (the failure
+ *                             mode the invariant policy removes); the values
+ *                             stay within the same accuracy of the exact ones.
+ */
+typedef enum bilogp_split_mode {
+  BILOGP_SPLITS_INVARIANT = 0,
+  BILOGP_SPLITS_THROUGHPUT = 1
+} bilogp_split_mode;
+
+#define BILOGP_MAX_THROUGHPUT_SPLITS 1024
+
+/* Tiles per split and split count under `mode` (cu_count is read only by the
+ * throughput mode, N only by it and for validity).  0 if N < 1 (throughput),
+ * V is out of range, mode is unknown or cu_count < 1 (throughput). */
+int bilogp_vtiles_per_split_mode(int64_t N, int64_t V, int mode, int cu_count);
+int bilogp_num_vocab_splits_mode(int64_t N, int64_t V, int mode, int cu_count);
+
+/* Workspace bytes for bilogp_forward_mode (as bilogp_workspace_bytes, with
+ * the mode's split count).  (size_t)-1 on invalid arguments, 0 for N == 0. */
+size_t bilogp_workspace_bytes_mode(int64_t N, int64_t V, int mode, int cu_count);
+
 /* Fused forward with an optional fp32 bias and a library-managed workspace
  * (stream-ordered hipMallocAsync / hipFreeAsync on `stream`).
  *
@@ -119,6 +155,18 @@ bilogp_status bilogp_forward_ex(const void* hidden, const void* weight, const in
                                 const void* bias, int bias_dtype, float* logp_out,
                                 float* lse_out, int64_t N, int64_t H, int64_t V,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* bilogp_forward_ex under split policy `mode` (BILOGP_SPLITS_INVARIANT gives
+ * exactly bilogp_forward_ex).  cu_count >= 1 is the compute-unit count the
+ * throughput policy fills (normally the device's); the workspace must hold
+ * bilogp_workspace_bytes_mode(N, V, mode, cu_count) bytes.  An unknown mode,
+ * or cu_count < 1 in throughput mode, gives BILOGP_E_INVALID_ARG.  At most
+ * BILOGP_MAX_THROUGHPUT_SPLITS splits are combined, in ascending order. */
+bilogp_status bilogp_forward_mode(const void* hidden, const void* weight, const int64_t* target,
+                                  const void* bias, int bias_dtype, float* logp_out,
+                                  float* lse_out, int64_t N, int64_t H, int64_t V, int mode,
+                                  int cu_count, void* workspace, size_t workspace_bytes,
+                                  void* stream);
 
 /* The two halves of bilogp_forward_ex, for callers that schedule them
  * separately (a timing harness, or a vocabulary-sharded caller that exchanges

@@ -30,30 +30,50 @@ from ._binding import (  # noqa: F401
     BILOGP_E_INVALID_ARG,
     BILOGP_E_UNSUPPORTED,
     BILOGP_E_WORKSPACE,
+    BILOGP_MAX_THROUGHPUT_SPLITS,
     BILOGP_OK,
+    BILOGP_SPLITS_INVARIANT,
+    BILOGP_SPLITS_THROUGHPUT,
     BilogpError,
     LIB_PATH,
     bilogp_abi_version,
     bilogp_forward,
     bilogp_forward_ex,
+    bilogp_forward_mode,
     bilogp_last_error,
     bilogp_max_splits,
     bilogp_merge,
     bilogp_num_vocab_splits,
+    bilogp_num_vocab_splits_mode,
     bilogp_partials,
     bilogp_status_string,
     bilogp_vtile_cols,
     bilogp_vtiles_per_split,
+    bilogp_vtiles_per_split_mode,
     bilogp_workspace_bytes,
+    bilogp_workspace_bytes_mode,
     load_library,
 )
 
-__all__ = ["forward", "workspace_for", "BilogpError", "load_library"]
+__all__ = ["forward", "workspace_for", "device_cu_count", "BilogpError", "load_library"]
 
 
-def workspace_for(N: int, V: int, device) -> Optional[torch.Tensor]:
-    """A uint8 device tensor big enough for ``bilogp_forward_ex`` (None if N == 0)."""
-    nbytes = bilogp_workspace_bytes(N, V)
+_SPLIT_MODES = {"invariant": BILOGP_SPLITS_INVARIANT, "throughput": BILOGP_SPLITS_THROUGHPUT}
+
+
+def device_cu_count(device) -> int:
+    """Compute units of a GPU (what the throughput split policy fills)."""
+    return torch.cuda.get_device_properties(torch.device(device)).multi_processor_count
+
+
+def workspace_for(N: int, V: int, device, split_mode: str = "invariant",
+                  cu_count: Optional[int] = None) -> Optional[torch.Tensor]:
+    """A uint8 device tensor big enough for ``bilogp_forward_ex`` (or, with
+    ``split_mode="throughput"``, ``bilogp_forward_mode``); None if N == 0."""
+    mode = _SPLIT_MODES[split_mode]
+    if mode == BILOGP_SPLITS_THROUGHPUT and cu_count is None:
+        cu_count = device_cu_count(device)
+    nbytes = bilogp_workspace_bytes_mode(N, V, mode, cu_count or 0)
     if nbytes == (1 << 64) - 1:
         raise ValueError(f"invalid sizes N={N}, V={V}")
     if nbytes == 0:
@@ -63,7 +83,8 @@ def workspace_for(N: int, V: int, device) -> Optional[torch.Tensor]:
 
 def forward(hidden: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
             bias: Optional[torch.Tensor] = None, *, check_targets: bool = True,
-            workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+            workspace: Optional[torch.Tensor] = None, split_mode: str = "invariant",
+            cu_count: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """(logp, lse), each fp32 with ``target``'s shape.
 
     hidden  [..., H] bf16        weight [V, H] bf16
@@ -73,7 +94,14 @@ def forward(hidden: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
 
     ``check_targets`` verifies 0 <= target < V on the host first (one device
     sync); without it an out-of-range target gives NaN for that row.
+
+    ``split_mode="throughput"`` chooses the vocabulary splits from N, V and
+    ``cu_count`` (default: the device's compute units) instead of V alone:
+    the same accuracy, but a row's bits then depend on the batch it is in.
+    It exists to measure what the invariant policy costs.
     """
+    if split_mode not in _SPLIT_MODES:
+        raise ValueError(f"split_mode must be one of {sorted(_SPLIT_MODES)}")
     if torch.is_grad_enabled() and (hidden.requires_grad or weight.requires_grad or
                                     (bias is not None and bias.requires_grad)):
         raise RuntimeError("batch-invariant linear logp is forward-only: call it under "
@@ -112,6 +140,14 @@ def forward(hidden: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
         logp = torch.empty(N, dtype=torch.float32, device=dev)
         lse = torch.empty(N, dtype=torch.float32, device=dev)
         if N > 0:
-            ws = workspace if workspace is not None else workspace_for(N, V, dev)
-            bilogp_forward_ex(hidden_2d, weight_2d, target_1d, bias_1d, logp, lse, ws)
+            mode = _SPLIT_MODES[split_mode]
+            if mode == BILOGP_SPLITS_INVARIANT:
+                ws = workspace if workspace is not None else workspace_for(N, V, dev)
+                bilogp_forward_ex(hidden_2d, weight_2d, target_1d, bias_1d, logp, lse, ws)
+            else:
+                cus = device_cu_count(dev) if cu_count is None else int(cu_count)
+                ws = workspace if workspace is not None else \
+                    workspace_for(N, V, dev, split_mode, cus)
+                bilogp_forward_mode(hidden_2d, weight_2d, target_1d, bias_1d, logp, lse, mode,
+                                    cus, ws)
     return logp.reshape(lead_shape), lse.reshape(lead_shape)

@@ -27,6 +27,10 @@ BILOGP_BIAS_NONE = 0
 BILOGP_BIAS_BF16 = 1
 BILOGP_BIAS_F32 = 2
 
+BILOGP_SPLITS_INVARIANT = 0
+BILOGP_SPLITS_THROUGHPUT = 1
+BILOGP_MAX_THROUGHPUT_SPLITS = 1024
+
 _STATUS_NAMES = {0: "BILOGP_OK", 1: "BILOGP_E_INVALID_ARG", 2: "BILOGP_E_UNSUPPORTED",
                  3: "BILOGP_E_WORKSPACE", 4: "BILOGP_E_HIP"}
 
@@ -40,6 +44,12 @@ SIGNATURES = {
     "bilogp_vtiles_per_split": (ctypes.c_int, [_I64]),
     "bilogp_num_vocab_splits": (ctypes.c_int, [_I64]),
     "bilogp_workspace_bytes": (ctypes.c_size_t, [_I64, _I64]),
+    "bilogp_vtiles_per_split_mode": (ctypes.c_int, [_I64, _I64, ctypes.c_int, ctypes.c_int]),
+    "bilogp_num_vocab_splits_mode": (ctypes.c_int, [_I64, _I64, ctypes.c_int, ctypes.c_int]),
+    "bilogp_workspace_bytes_mode": (ctypes.c_size_t, [_I64, _I64, ctypes.c_int, ctypes.c_int]),
+    "bilogp_forward_mode": (ctypes.c_int, [_VP, _VP, _VP, _VP, ctypes.c_int, _VP, _VP, _I64, _I64,
+                                           _I64, ctypes.c_int, ctypes.c_int, _VP,
+                                           ctypes.c_size_t, _VP]),
     "bilogp_forward": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _VP]),
     "bilogp_forward_ex": (ctypes.c_int, [_VP, _VP, _VP, _VP, ctypes.c_int, _VP, _VP, _I64, _I64,
                                          _I64, _VP, ctypes.c_size_t, _VP]),
@@ -124,6 +134,18 @@ def bilogp_workspace_bytes(N: int, V: int) -> int:
     return load_library().bilogp_workspace_bytes(N, V)
 
 
+def bilogp_vtiles_per_split_mode(N: int, V: int, mode: int, cu_count: int) -> int:
+    return load_library().bilogp_vtiles_per_split_mode(N, V, mode, cu_count)
+
+
+def bilogp_num_vocab_splits_mode(N: int, V: int, mode: int, cu_count: int) -> int:
+    return load_library().bilogp_num_vocab_splits_mode(N, V, mode, cu_count)
+
+
+def bilogp_workspace_bytes_mode(N: int, V: int, mode: int, cu_count: int) -> int:
+    return load_library().bilogp_workspace_bytes_mode(N, V, mode, cu_count)
+
+
 def bilogp_status_string(status: int) -> str:
     return load_library().bilogp_status_string(status).decode()
 
@@ -174,6 +196,24 @@ def bilogp_forward_ex(hidden: torch.Tensor, weight: torch.Tensor, target: torch.
                                    _bias_dtype(bias), _ptr(logp_out), _ptr(lse_out), N, H, V,
                                    _ptr(workspace), ws_bytes,
                                    _stream_handle(stream, hidden.device))
+    _check(st)
+
+
+def bilogp_forward_mode(hidden: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
+                        bias: Optional[torch.Tensor], logp_out: torch.Tensor,
+                        lse_out: torch.Tensor, mode: int, cu_count: int,
+                        workspace: Optional[torch.Tensor], stream=None) -> None:
+    """``bilogp_forward_mode``: ``bilogp_forward_ex`` under split policy
+    ``mode`` with ``cu_count`` compute units for the throughput policy."""
+    N, H = hidden.shape
+    V = weight.shape[0]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib = load_library()
+    with torch.cuda.device(hidden.device):
+        st = lib.bilogp_forward_mode(_ptr(hidden), _ptr(weight), _ptr(target), _ptr(bias),
+                                     _bias_dtype(bias), _ptr(logp_out), _ptr(lse_out), N, H, V,
+                                     mode, cu_count, _ptr(workspace), ws_bytes,
+                                     _stream_handle(stream, hidden.device))
     _check(st)
 
 

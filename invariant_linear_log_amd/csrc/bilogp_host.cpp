@@ -14,6 +14,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <string>
 
@@ -133,9 +134,34 @@ int bilogp_num_vocab_splits(int64_t V) {
 }
 
 size_t bilogp_workspace_bytes(int64_t N, int64_t V) {
-  const int S = bilogp_num_vocab_splits(V);
-  if (N < 0 || N > kMaxN || S == 0) return (size_t)-1;
-  if (N == 0) return 0;
+  return bilogp_workspace_bytes_mode(N, V, BILOGP_SPLITS_INVARIANT, 0);
+}
+
+int bilogp_vtiles_per_split_mode(int64_t N, int64_t V, int mode, int cu_count) {
+  if (mode == BILOGP_SPLITS_INVARIANT) return bilogp_vtiles_per_split(V);
+  if (mode != BILOGP_SPLITS_THROUGHPUT) return 0;
+  if (N < 1 || N > kMaxN || V <= 0 || V > kMaxV || cu_count < 1) return 0;
+  // want = min(max(ceil(cu / R), 1), T, cap); per_split = ceil(T / want)
+  const int64_t tiles = (V + bilogp::kVtileCols - 1) / bilogp::kVtileCols;
+  const int64_t row_blocks = (N + bilogp::kBlockRows - 1) / bilogp::kBlockRows;
+  int64_t want = ((int64_t)cu_count + row_blocks - 1) / row_blocks;
+  want = std::min(std::max<int64_t>(want, 1), std::min<int64_t>(tiles, bilogp::kMaxThroughputSplits));
+  return (int)((tiles + want - 1) / want);
+}
+
+int bilogp_num_vocab_splits_mode(int64_t N, int64_t V, int mode, int cu_count) {
+  const int per_split = bilogp_vtiles_per_split_mode(N, V, mode, cu_count);
+  if (per_split == 0) return 0;
+  const int64_t tiles = (V + bilogp::kVtileCols - 1) / bilogp::kVtileCols;
+  return (int)((tiles + per_split - 1) / per_split);
+}
+
+size_t bilogp_workspace_bytes_mode(int64_t N, int64_t V, int mode, int cu_count) {
+  if (N < 0 || N > kMaxN) return (size_t)-1;
+  if (mode != BILOGP_SPLITS_INVARIANT && mode != BILOGP_SPLITS_THROUGHPUT) return (size_t)-1;
+  if (N == 0) return (V > 0 && V <= kMaxV) ? 0 : (size_t)-1;
+  const int S = bilogp_num_vocab_splits_mode(N, V, mode, cu_count);
+  if (S == 0) return (size_t)-1;
   return round_up((size_t)N * (size_t)S * sizeof(float2)) + round_up((size_t)N * sizeof(float)) +
          round_up(padded_vocab(V) * sizeof(float));
 }
@@ -172,6 +198,8 @@ struct Call {
   int64_t N, H, V;
   void* ws;
   size_t ws_bytes;
+  int mode = BILOGP_SPLITS_INVARIANT;
+  int cu_count = 0;
 };
 
 // Full argument validation (fail closed) and the launch parameters.  Pure
@@ -184,6 +212,10 @@ bilogp_status validate(const Call& c, int parts, bilogp::ProjParams* out) {
   if (proj && (c.H <= 0 || c.H > kMaxH))
     return fail(BILOGP_E_INVALID_ARG, "H out of range [1, 2^20]");
   if (c.V <= 0 || c.V > kMaxV) return fail(BILOGP_E_INVALID_ARG, "V out of range [1, 2^30]");
+  if (c.mode != BILOGP_SPLITS_INVARIANT && c.mode != BILOGP_SPLITS_THROUGHPUT)
+    return fail(BILOGP_E_INVALID_ARG, "unknown split mode");
+  if (c.mode == BILOGP_SPLITS_THROUGHPUT && c.cu_count < 1)
+    return fail(BILOGP_E_INVALID_ARG, "the throughput split mode needs cu_count >= 1");
   size_t bias_esz = 0;
   if (proj) {
     if (c.bias_dtype != BILOGP_BIAS_NONE && c.bias_dtype != BILOGP_BIAS_BF16 &&
@@ -204,7 +236,7 @@ bilogp_status validate(const Call& c, int parts, bilogp::ProjParams* out) {
     return fail(BILOGP_E_UNSUPPORTED, "outputs must be 4-byte aligned");
   if (c.N == 0) return BILOGP_OK;
 
-  const int S = bilogp_num_vocab_splits(c.V);
+  const int S = bilogp_num_vocab_splits_mode(c.N, c.V, c.mode, c.cu_count);
   const int64_t R = (c.N + bilogp::kBlockRows - 1) / bilogp::kBlockRows;
   if (R * S > INT32_MAX) return fail(BILOGP_E_INVALID_ARG, "N too large for one launch");
 
@@ -222,7 +254,7 @@ bilogp_status validate(const Call& c, int parts, bilogp::ProjParams* out) {
         return fail(BILOGP_E_INVALID_ARG, "an output overlaps an input or the workspace");
   }
 
-  const size_t need = bilogp_workspace_bytes(c.N, c.V);
+  const size_t need = bilogp_workspace_bytes_mode(c.N, c.V, c.mode, c.cu_count);
   if (!c.ws || c.ws_bytes < need)
     return fail(BILOGP_E_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
   if (reinterpret_cast<uintptr_t>(c.ws) % kAlign != 0)
@@ -256,7 +288,7 @@ bilogp_status validate(const Call& c, int parts, bilogp::ProjParams* out) {
                 : c.bias_dtype == BILOGP_BIAS_F32 ? bilogp::kBiasF32
                                                   : bilogp::kBiasNone;
   p.T = (int32_t)((c.V + bilogp::kVtileCols - 1) / bilogp::kVtileCols);
-  p.vps = bilogp_vtiles_per_split(c.V);
+  p.vps = bilogp_vtiles_per_split_mode(c.N, c.V, c.mode, c.cu_count);
   p.S = S;
   p.R = (int32_t)R;
   return BILOGP_OK;
@@ -303,6 +335,18 @@ bilogp_status bilogp_forward_ex(const void* hidden, const void* weight, const in
                                 void* workspace, size_t workspace_bytes, void* stream) {
   const Call c{hidden, weight, target, bias, bias_dtype, logp_out, lse_out,
                N,      H,      V,      workspace, workspace_bytes};
+  return run(c, kProj | kMerge, stream);
+}
+
+bilogp_status bilogp_forward_mode(const void* hidden, const void* weight, const int64_t* target,
+                                  const void* bias, int bias_dtype, float* logp_out,
+                                  float* lse_out, int64_t N, int64_t H, int64_t V, int mode,
+                                  int cu_count, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  Call c{hidden, weight, target, bias, bias_dtype, logp_out, lse_out,
+         N,      H,      V,      workspace, workspace_bytes};
+  c.mode = mode;
+  c.cu_count = cu_count;
   return run(c, kProj | kMerge, stream);
 }
 

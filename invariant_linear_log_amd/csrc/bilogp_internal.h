@@ -11,6 +11,9 @@ namespace bilogp {
 constexpr int kVtileCols = 256;
 constexpr int kMaxSplits = 64;
 
+// Cap of the throughput split policy (not part of the invariant contract).
+constexpr int kMaxThroughputSplits = 1024;
+
 // Tokens handled by one projection workgroup.  Internal only: a row's
 // arithmetic does not depend on it (no reduction mixes rows).
 constexpr int kBlockRows = 256;

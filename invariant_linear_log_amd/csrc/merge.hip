@@ -6,10 +6,13 @@
 // an ascending combine; the same splits for every N).
 //
 // One wave64 per row; lane k holds split k (S <= 64 = wave width, the
-// library's split limit).  M = max_k m_k is exact in any order.  The terms
-// s_k * exp(m_k - M) are summed by a pairwise tree over ascending split
+// invariant policy's split limit).  M = max_k m_k is exact in any order.  The
+// terms s_k * exp(m_k - M) are summed by a pairwise tree over ascending split
 // index: (s0 + s1), (s2 + s3), ..., then ((s0 + s1) + (s2 + s3)), ... - the
-// same tree for every row and every N.  With a max-element term of exactly
+// same tree for every row and every N.  The throughput split policy can give
+// up to 1024 splits: lane k then first adds the terms of splits k, k + 64,
+// k + 128, ... in ascending order, and the tree combines the 64 lane sums
+// (for S <= 64 this is the same computation: 0 + x == x).  With a max-element term of exactly
 // 1 the sum is >= 1, so lse >= M >= z_target and logp <= 0 exactly.
 //
 // logp = (z_target - M) - ln(sum), lse = M + ln(sum).  A target outside
@@ -36,17 +39,17 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void merge_kernel(
   const int lane = threadIdx.x & 63;
   if (row >= N) return;                     // uniform across the wave
 
-  float m = -INFINITY, s = 0.f;
-  if (lane < S) {
-    const float2 ps = part[row * S + lane];
-    m = ps.x;
-    s = ps.y;
-  }
-  float M = m;
+  const float2* pr = part + row * S;
+  float M = -INFINITY;
+  for (int k = lane; k < S; k += 64) M = fmaxf(M, pr[k].x);
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d));
   const float mu = (M == -INFINITY) ? 0.f : M;
-  float term = (lane < S) ? s * __builtin_amdgcn_exp2f((m - mu) * kLog2e) : 0.f;
+  float term = 0.f;
+  for (int k = lane; k < S; k += 64) {
+    const float2 ps = pr[k];
+    term += ps.y * __builtin_amdgcn_exp2f((ps.x - mu) * kLog2e);
+  }
   // lane k and lane k^d add the same two operands, so every lane of a group
   // carries identical bits after each level
 #pragma unroll

@@ -15,6 +15,8 @@ linear_logp
     ``decode_bf16``               exact bf16 -> float64 decode from the bit pattern
     ``linear_logp``               the plain definition (dgemm + explicit max / exp / log)
     ``vocab_splits``              the V-only contiguous split policy
+    ``vocab_splits_throughput``   a split policy from N, V and the compute-unit count
+                                  (the throughput scheduling the method replaces)
     ``split_merge_linear_logp``   the method's own steps: per-split online
                                   (max, sum-exp) partials, then the ascending combine
     ``brute_force_linear_logp``   pure-Python ``math.fsum`` version for tiny inputs
@@ -25,6 +27,7 @@ from .linear_logp import (  # noqa: F401
     to_f64,
     linear_logp,
     vocab_splits,
+    vocab_splits_throughput,
     split_merge_linear_logp,
     brute_force_linear_logp,
 )

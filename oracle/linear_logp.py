@@ -47,6 +47,7 @@ __all__ = [
     "to_f64",
     "linear_logp",
     "vocab_splits",
+    "vocab_splits_throughput",
     "split_merge_linear_logp",
     "brute_force_linear_logp",
 ]
@@ -169,9 +170,37 @@ def vocab_splits(V: int, vtile: int, max_splits: int) -> list:
     return [(k * per_split, min((k + 1) * per_split, tiles)) for k in range(n_splits)]
 
 
+def vocab_splits_throughput(N: int, V: int, cu_count: int, vtile: int = 256,
+                            block_rows: int = 256, max_splits: int = 1024) -> list:
+    """Contiguous vocabulary-tile ranges chosen from N, V and the number of
+    compute units: the throughput-oriented scheduling that the invariant
+    policy replaces.
+
+    PR #337, description ("Why this happens" and its flowchart): the existing
+    fused operator's throughput scheduler picks the vocabulary split from N, V
+    and the GPU's SM count, so one token row can be reduced as [A][B][C][D]
+    inside one batch and as [A B][C D] inside another.  The page does not give
+    that scheduler's formula; this is the plainest policy of that kind: enough
+    splits that ceil(N / block_rows) row blocks times the split count reach
+    the compute-unit count, at most ``max_splits`` and at most one per tile,
+    every split (but the last) taking the same number of tiles.  Returns
+    half-open tile ranges (first_tile, end_tile).
+    """
+    if N <= 0 or V <= 0 or cu_count <= 0 or vtile <= 0 or block_rows <= 0 or max_splits <= 0:
+        raise ValueError("N, V, cu_count, vtile, block_rows and max_splits must be positive")
+    tiles = -(-V // vtile)
+    row_blocks = -(-N // block_rows)
+    want = min(max(-(-cu_count // row_blocks), 1), tiles, max_splits)
+    per_split = -(-tiles // want)
+    n_splits = -(-tiles // per_split)
+    return [(k * per_split, min((k + 1) * per_split, tiles)) for k in range(n_splits)]
+
+
 def split_merge_linear_logp(hidden, weight, target, bias=None, vtile: int = 256,
                             max_splits: int = 64,
-                            rows: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+                            rows: Optional[Sequence[int]] = None,
+                            splits: Optional[Sequence[Tuple[int, int]]] = None
+                            ) -> Tuple[np.ndarray, np.ndarray]:
     """(logp, lse) in float64 following the method's steps in the page's order
     (PR #337, description, "What this PR changes"):
 
@@ -186,6 +215,8 @@ def split_merge_linear_logp(hidden, weight, target, bias=None, vtile: int = 256,
 
     In real arithmetic this equals ``linear_logp``; in float64 the two agree to
     rounding, which pins the combine algebra independently of any GPU code.
+    ``splits`` replaces step 1 by an explicit list of contiguous tile ranges
+    (for instance ``vocab_splits_throughput``); the combine is unchanged.
     """
     h = to_f64(hidden)
     w = to_f64(weight)
@@ -197,7 +228,14 @@ def split_merge_linear_logp(hidden, weight, target, bias=None, vtile: int = 256,
     tr = t[idx]
     R = idx.shape[0]
     V = w.shape[0]
-    splits = vocab_splits(V, vtile, max_splits)
+    if splits is None:
+        splits = vocab_splits(V, vtile, max_splits)
+    tiles = -(-V // vtile)
+    ok = (len(splits) > 0 and splits[0][0] == 0 and splits[-1][1] == tiles
+          and all(a < b for a, b in splits)
+          and all(splits[i][1] == splits[i + 1][0] for i in range(len(splits) - 1)))
+    if not ok:
+        raise ValueError("splits must be non-empty contiguous tile ranges covering [0, T)")
 
     part_m = np.empty((len(splits), R))
     part_s = np.empty((len(splits), R))

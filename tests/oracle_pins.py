@@ -279,6 +279,40 @@ def pin_split_policy(orc):
     _assert(len(r) == 33 and r[-1] == (64, 65), "V=16385 splits")
 
 
+def pin_throughput_policy(orc):
+    """The N / V / compute-unit split policy: ranges contiguous, non-empty,
+    covering all tiles, even-sized, at most min(tiles, 1024) of them, and at
+    least half the count that would fill the compute units (per_split =
+    ceil(T / want) gives S >= want / 2 whenever T >= want); plus worked values."""
+    for N in (1, 8, 255, 256, 257, 512, 4096, 16384, 100000):
+        for V in (1, 255, 1000, 32000, 128256, 151936):
+            for cu in (1, 3, 80, 256, 304, 5000):
+                r = orc.vocab_splits_throughput(N, V, cu)
+                tiles, R = -(-V // 256), -(-N // 256)
+                _assert(r[0][0] == 0 and r[-1][1] == tiles, f"cover N={N} V={V} cu={cu}")
+                _assert(all(a < b for a, b in r), f"empty split N={N} V={V} cu={cu}")
+                _assert(all(r[i][1] == r[i + 1][0] for i in range(len(r) - 1)), "gap")
+                sizes = [b - a for a, b in r]
+                _assert(all(x == sizes[0] for x in sizes[:-1]) and sizes[-1] <= sizes[0], "uneven")
+                want = min(-(-cu // R), tiles, 1024)
+                _assert(want / 2 <= len(r) <= want, f"count N={N} V={V} cu={cu}: {len(r)} vs {want}")
+    # worked values (T = ceil(V / 256), R = ceil(N / 256), want = min(ceil(cu / R), T, 1024))
+    r = orc.vocab_splits_throughput(4096, 128256, 256)      # R 16, want 16, 32 per split
+    _assert(len(r) == 16 and r[0] == (0, 32) and r[-1] == (480, 501), "N=4096 V=128256")
+    r = orc.vocab_splits_throughput(512, 128256, 256)       # R 2, want 128, 4 per split
+    _assert(len(r) == 126 and r[-1] == (500, 501), "N=512 V=128256")
+    r = orc.vocab_splits_throughput(8, 128256, 256)         # R 1, want 256, 2 per split
+    _assert(len(r) == 251 and r[-1] == (500, 501), "N=8 V=128256")
+    r = orc.vocab_splits_throughput(8, 1000, 256)           # want capped by the 4 tiles
+    _assert(r == [(0, 1), (1, 2), (2, 3), (3, 4)], "N=8 V=1000")
+    r = orc.vocab_splits_throughput(16384, 152064, 256)     # R 64, want 4, 149 per split
+    _assert(len(r) == 4 and r[-1] == (447, 594), "N=16384 V=152064")
+    r = orc.vocab_splits_throughput(16384, 152064, 304)     # R 64, want ceil(4.75) = 5
+    _assert(len(r) == 5 and r[0] == (0, 119) and r[-1] == (476, 594), "N=16384 cu=304")
+    r = orc.vocab_splits_throughput(1, 2 ** 30, 5000)       # want capped at 1024
+    _assert(len(r) == 1024 and r[0] == (0, 4096), "cap 1024")
+
+
 # ---------------------------------------------------------------- pin 11
 def pin_split_merge_equals_plain(orc):
     """The method's split / online / ascending-combine steps equal the plain
@@ -293,6 +327,15 @@ def pin_split_merge_equals_plain(orc):
                                                inp["bias"], vtile=vt, max_splits=mx)
         _assert(_maxabs(lp1, lp2) <= 1e-12 and _maxabs(ls1, ls2) <= 1e-12,
                 f"split-merge vs plain case {j}: {_maxabs(lp1, lp2)} {_maxabs(ls1, ls2)}")
+    # the same steps over throughput-mode partitions (more, smaller splits)
+    for j, (N, H, V, cu) in enumerate([(3, 16, 5000, 64), (2, 8, 70001, 256), (5, 16, 1000, 3)]):
+        inp = synth.make_custom(N, H, V, seed=70 + j, bias="bf16" if j % 2 else None)
+        lp1, ls1 = orc.linear_logp(inp["hidden"], inp["weight"], inp["target"], inp["bias"])
+        lp2, ls2 = orc.split_merge_linear_logp(inp["hidden"], inp["weight"], inp["target"],
+                                               inp["bias"],
+                                               splits=orc.vocab_splits_throughput(N, V, cu))
+        _assert(_maxabs(lp1, lp2) <= 1e-12 and _maxabs(ls1, ls2) <= 1e-12,
+                f"throughput split-merge vs plain case {j}")
 
 
 # ---------------------------------------------------------------- pin 12
@@ -311,5 +354,5 @@ def pin_row_subset(orc):
 ALL_PINS = [pin_decode, pin_worked_example, pin_brute_force, pin_brute_force_mpmath,
             pin_log_softmax_library, pin_w0_closed_form, pin_w0_bias, pin_bias_shift,
             pin_normalisation, pin_sign_and_argmax, pin_large_logits, pin_large_logit_spread,
-            pin_split_policy,
+            pin_split_policy, pin_throughput_policy,
             pin_split_merge_equals_plain, pin_row_subset]

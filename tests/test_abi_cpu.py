@@ -57,6 +57,47 @@ def test_split_policy_matches_oracle():
         assert ila.bilogp_vtiles_per_split(V) == ranges[0][1] - ranges[0][0], V
 
 
+def test_throughput_policy_matches_oracle():
+    inv, tp = B.BILOGP_SPLITS_INVARIANT, B.BILOGP_SPLITS_THROUGHPUT
+    for N in (1, 8, 255, 256, 257, 512, 1000, 4096, 16384, 2 ** 20):
+        for V in (1, 255, 1000, 5003, 32000, 70001, 128256, 151936, 2 ** 30):
+            for cu in (1, 3, 80, 256, 304, 5000):
+                ranges = oracle.vocab_splits_throughput(N, V, cu, vtile=256, block_rows=256,
+                                                        max_splits=B.BILOGP_MAX_THROUGHPUT_SPLITS)
+                assert ila.bilogp_num_vocab_splits_mode(N, V, tp, cu) == len(ranges), (N, V, cu)
+                assert ila.bilogp_vtiles_per_split_mode(N, V, tp, cu) == \
+                    ranges[0][1] - ranges[0][0], (N, V, cu)
+            # the invariant mode ignores N and the compute units
+            assert ila.bilogp_num_vocab_splits_mode(N, V, inv, 7) == ila.bilogp_num_vocab_splits(V)
+            assert ila.bilogp_vtiles_per_split_mode(N, V, inv, 0) == ila.bilogp_vtiles_per_split(V)
+
+
+def test_throughput_policy_invalid():
+    tp = B.BILOGP_SPLITS_THROUGHPUT
+    for N, V, mode, cu in [(0, 1000, tp, 256), (-1, 1000, tp, 256), (8, 0, tp, 256),
+                           (8, 1000, tp, 0), (8, 1000, 2, 256), (8, 1000, -1, 256),
+                           (8, 2 ** 30 + 1, tp, 256)]:
+        assert ila.bilogp_num_vocab_splits_mode(N, V, mode, cu) == 0, (N, V, mode, cu)
+        assert ila.bilogp_vtiles_per_split_mode(N, V, mode, cu) == 0, (N, V, mode, cu)
+
+
+def test_workspace_bytes_mode():
+    def up(x):
+        return (x + 255) // 256 * 256
+    tp = B.BILOGP_SPLITS_THROUGHPUT
+    for N, V, cu in [(1, 1000, 256), (8, 128256, 256), (512, 128256, 256), (4096, 128256, 80)]:
+        S = len(oracle.vocab_splits_throughput(N, V, cu))
+        padded = (V + 255) // 256 * 256
+        assert ila.bilogp_workspace_bytes_mode(N, V, tp, cu) == up(8 * N * S) + up(4 * N) + \
+            up(4 * padded)
+        assert ila.bilogp_workspace_bytes_mode(N, V, B.BILOGP_SPLITS_INVARIANT, cu) == \
+            ila.bilogp_workspace_bytes(N, V)
+    big = (1 << 64) - 1
+    assert ila.bilogp_workspace_bytes_mode(0, 1000, tp, 256) == 0
+    assert ila.bilogp_workspace_bytes_mode(8, 1000, tp, 0) == big
+    assert ila.bilogp_workspace_bytes_mode(8, 1000, 5, 256) == big
+
+
 def test_split_policy_out_of_range():
     for V in (0, -1, 2 ** 30 + 1, 2 ** 40):
         assert ila.bilogp_num_vocab_splits(V) == 0
@@ -121,6 +162,31 @@ def test_forward_ex_fails_closed(kw, status):
     st = _call_ex(**kw)
     assert st == status, (st, ila.bilogp_last_error())
     assert ila.bilogp_last_error() != ""
+
+
+@pytest.mark.parametrize("mode,cu,status", [
+    (2, 256, B.BILOGP_E_INVALID_ARG),           # unknown mode
+    (-1, 256, B.BILOGP_E_INVALID_ARG),
+    (B.BILOGP_SPLITS_THROUGHPUT, 0, B.BILOGP_E_INVALID_ARG),   # no compute units
+    (B.BILOGP_SPLITS_THROUGHPUT, -5, B.BILOGP_E_INVALID_ARG),
+])
+def test_forward_mode_fails_closed(mode, cu, status):
+    lib = ila.load_library()
+    st = lib.bilogp_forward_mode(FAKE, FAKE + 0x100000, FAKE + 0x200000, None, 0, FAKE + 0x300000,
+                                 FAKE + 0x400000, 8, 64, 1000, mode, cu, FAKE + 0x500000, 1 << 20,
+                                 None)
+    assert st == status, (st, ila.bilogp_last_error())
+
+
+def test_forward_mode_workspace_is_per_mode():
+    # enough for the invariant mode's 63 splits of V=128256, but the throughput
+    # mode at N=8 takes 251: the size check uses the mode's own split count
+    lib = ila.load_library()
+    need_inv = ila.bilogp_workspace_bytes(8, 128256)
+    st = lib.bilogp_forward_mode(FAKE, FAKE + 0x10000000, FAKE + 0x200000, None, 0, FAKE + 0x300000,
+                                 FAKE + 0x400000, 8, 64, 128256, B.BILOGP_SPLITS_THROUGHPUT, 256,
+                                 FAKE + 0x40000000, need_inv, None)
+    assert st == B.BILOGP_E_WORKSPACE, (st, ila.bilogp_last_error())
 
 
 def test_empty_batch_is_a_noop():

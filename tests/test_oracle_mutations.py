@@ -34,6 +34,10 @@ MUTATIONS = {
     "combine_max_not_global": ("M = part_m.max(axis=0)", "M = part_m[0]"),
     "brute_no_bias": ("            if b is not None:\n                terms.append(b[v])\n", ""),
     "brute_lse_shift_lost": ("lse = zmax + math.log(", "lse = math.log("),
+    "throughput_row_blocks_floor": ("row_blocks = -(-N // block_rows)", "row_blocks = max(1, N // block_rows)"),
+    "throughput_cu_floor": ("-(-cu_count // row_blocks)", "(cu_count // row_blocks)"),
+    "throughput_no_max_cap": ("want = min(max(-(-cu_count // row_blocks), 1), tiles, max_splits)",
+                              "want = min(max(-(-cu_count // row_blocks), 1), tiles)"),
 }
 
 

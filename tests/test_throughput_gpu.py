@@ -1,0 +1,112 @@
+"""The throughput split mode: vocabulary splits chosen from N, V and a
+compute-unit count instead of V alone.  It must be as accurate as the
+invariant mode (same oracle, same 2e-3 bar), and - the contrast the method is
+about - its bits depend on the batch a row sits in (RL-Kernel PR #337,
+description, "Why this happens": the throughput scheduler may reduce the same
+row as [A][B][C][D] inside one batch and as [A B][C D] inside another).
+Small N with many compute units gives more than 64 splits, which exercises the
+merge's per-lane ascending pre-sum."""
+
+import pytest
+import torch
+
+import invariant_linear_log_amd as ila
+import oracle
+import synth
+from gpu_common import DEV, assert_parity, flat, oracle_rows, run_ex, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+TP = ila.BILOGP_SPLITS_THROUGHPUT
+INV = ila.BILOGP_SPLITS_INVARIANT
+
+
+def run_mode(h, w, t, b, mode, cu):
+    N, V = h.shape[0], w.shape[0]
+    logp = torch.empty(N, dtype=torch.float32, device=DEV)
+    lse = torch.empty(N, dtype=torch.float32, device=DEV)
+    ws = ila.workspace_for(N, V, DEV, "throughput" if mode == TP else "invariant", cu)
+    ila.bilogp_forward_mode(h, w, t, b, logp, lse, mode, cu, ws)
+    return logp, lse
+
+
+# (N, H, V, bias, seed, cu): splits S from the policy noted on the right
+CASES = [
+    (8, 64, 1000, None, 0, 256),          # T 4: 4 splits of one tile
+    (512, 1024, 32000, "f32", 1, 256),    # T 125, R 2: 125 splits (> 64)
+    (777, 520, 70001, "bf16", 2, 80),     # T 274, R 4: 20 splits of 14 tiles
+    (1000, 1000, 5003, None, 3, 304),     # T 20, R 4: 20 splits
+    (300, 264, 16385, "bf16", 4, 1000),   # T 65, R 2: 65 splits (> 64)
+]
+
+
+@pytest.mark.parametrize("N,H,V,bias,seed,cu", CASES)
+def test_throughput_parity_full(N, H, V, bias, seed, cu):
+    inp = synth.make_custom(N, H, V, seed=40 + seed, bias=bias, device=DEV)
+    h, t = flat(inp)
+    S = ila.bilogp_num_vocab_splits_mode(N, V, TP, cu)
+    assert S == len(oracle.vocab_splits_throughput(N, V, cu))
+    say(f"throughput N={N} H={H} V={V} bias={bias} cu={cu} S={S}")
+    logp, lse = run_mode(h, inp["weight"], t, inp["bias"], TP, cu)
+    torch.cuda.synchronize()
+    ref_lp, ref_ls = oracle_rows(inp)
+    assert_parity(logp, lse, ref_lp, ref_ls, what=f"throughput S={S}")
+
+
+def test_throughput_251_splits_headline_rows():
+    """Eight headline rows alone: one row block, 256 compute units -> 251
+    splits of two tiles, merged by the strided per-lane pre-sum."""
+    inp = synth.make_inputs("headline", device=DEV)
+    h, t = flat(inp)
+    h8, t8 = h[:8].contiguous(), t[:8].contiguous()
+    assert ila.bilogp_num_vocab_splits_mode(8, 128256, TP, 256) == 251
+    say("headline 8 rows, throughput, 251 splits")
+    logp, lse = run_mode(h8, inp["weight"], t8, None, TP, 256)
+    torch.cuda.synchronize()
+    ref_lp, ref_ls = oracle.linear_logp(h8.cpu(), inp["weight"].cpu(), t8.cpu())
+    assert_parity(logp, lse, ref_lp, ref_ls, what="throughput 251 splits")
+
+
+def test_throughput_headline_sampled():
+    inp = synth.make_inputs("headline", device=DEV)
+    h, t = flat(inp)
+    say("headline N=4096, throughput, 16 splits")
+    logp, lse = run_mode(h, inp["weight"], t, None, TP, ila.device_cu_count(DEV))
+    torch.cuda.synchronize()
+    rows = sample_rows(4096, 128, seed=21)
+    ref_lp, ref_ls = oracle_rows(inp, rows=rows)
+    assert_parity(logp, lse, ref_lp, ref_ls, rows=rows, what="throughput headline")
+
+
+def test_invariant_mode_is_forward_ex():
+    inp = synth.make_inputs("medium", device=DEV)
+    h, t = flat(inp)
+    say("forward_mode(invariant) vs forward_ex, medium")
+    a_lp, a_ls = run_mode(h, inp["weight"], t, inp["bias"], INV, 1)
+    b_lp, b_ls = run_ex(h, inp["weight"], t, inp["bias"])
+    torch.cuda.synchronize()
+    assert torch.equal(a_lp, b_lp) and torch.equal(a_ls, b_ls)
+
+
+def test_throughput_bits_depend_on_the_batch():
+    """The same 64 headline rows, run inside the full 4096-row batch and on
+    their own: the throughput mode cuts the vocabulary differently (16 vs 251
+    splits), so the bits change while the values stay within the accuracy
+    bar; the invariant mode gives identical bits."""
+    inp = synth.make_inputs("headline", device=DEV)
+    h, t = flat(inp)
+    w = inp["weight"]
+    cu = ila.device_cu_count(DEV)
+    say("throughput vs invariant: rows inside N=4096 and alone")
+    tp_full_lp, tp_full_ls = run_mode(h, w, t, None, TP, cu)
+    tp_part_lp, tp_part_ls = run_mode(h[:64].contiguous(), w, t[:64].contiguous(), None, TP, cu)
+    inv_full_lp, inv_full_ls = run_ex(h, w, t)
+    inv_part_lp, inv_part_ls = run_ex(h[:64].contiguous(), w, t[:64].contiguous())
+    torch.cuda.synchronize()
+    assert ila.bilogp_num_vocab_splits_mode(4096, 128256, TP, cu) != \
+        ila.bilogp_num_vocab_splits_mode(64, 128256, TP, cu)
+    assert torch.equal(inv_part_lp, inv_full_lp[:64]) and torch.equal(inv_part_ls, inv_full_ls[:64])
+    assert not torch.equal(tp_part_ls, tp_full_ls[:64]), "throughput bits did not move with N"
+    d = float((tp_part_ls.double() - tp_full_ls[:64].double()).abs().max())
+    say(f"throughput lse drift between batches: {d:.3e}")
+    assert d <= 2e-3
