@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-det-gemm", action="store_true",
+                    help="skip timing the deterministic GEMM (forward, dA, dB)")
     ap.add_argument("--no-invariance-cost", action="store_true",
                     help="skip timing the throughput split policy beside the invariant one")
     ap.add_argument("--cpu-rows", type=int, default=4096,
@@ -119,6 +121,42 @@ def invariance_cost(h, t, w, b, steps=10, warmup=3):
             res[f"n{n}_{name}_ms"] = e0.elapsed_time(e1) / steps
             res[f"n{n}_{name}_splits"] = ila.bilogp_num_vocab_splits_mode(n, V, mode, cu)
     return res
+
+
+def det_gemm_leg(steps=10, warmup=3):
+    """The deterministic GEMM (forward, dA, dB) at M = N = K = 4096 and at the
+    largest shape of the page's own table (M, K, N = 512, 1024, 1024), with
+    torch's bf16 matmul (hipBLASLt, not deterministic by contract) beside it."""
+    import torch
+    import invariant_linear_log_amd as ila
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(11)
+    out = {"peak_tflops": PEAK_BF16_TFLOPS}
+    for (M, N, K) in ((4096, 4096, 4096), (512, 1024, 1024)):
+        a = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+        b = torch.randn((N, K), generator=g, device=dev).to(torch.bfloat16)
+        dc = torch.randn((M, N), generator=g, device=dev).to(torch.bfloat16)
+        bt = b.t().contiguous()              # [K, N] once, outside the timed calls
+        flops = 2.0 * M * N * K
+        runs = {"fwd": lambda: ila.det_gemm(a, b), "da": lambda: ila.det_gemm_da(dc, b),
+                "db": lambda: ila.det_gemm_db(a, dc),
+                "torch_matmul_fwd": lambda: torch.matmul(a, bt)}
+        rec = {}
+        for name, fn in runs.items():
+            for _ in range(warmup):
+                fn()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                fn()
+            e1.record()
+            e1.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            rec[name] = {"ms": ms, "tflops": flops / ms / 1e9}
+        rec["fwd"]["frac"] = rec["fwd"]["tflops"] / PEAK_BF16_TFLOPS
+        out[f"M{M}_N{N}_K{K}"] = rec
+    return out
 
 
 def cpu_baseline(inp, rows_n, seed=7):
@@ -239,6 +277,8 @@ def main():
     }
     if not args.no_invariance_cost:
         out["invariance_cost"] = invariance_cost(h, t, w, b)
+    if not args.no_det_gemm:
+        out["det_gemm"] = det_gemm_leg()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows)
     print(json.dumps(out), flush=True)

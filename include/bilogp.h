@@ -188,6 +188,44 @@ bilogp_status bilogp_partials(const void* hidden, const void* weight, const int6
 bilogp_status bilogp_merge(const int64_t* target, const void* workspace, size_t workspace_bytes,
                            float* logp_out, float* lse_out, int64_t N, int64_t V, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Deterministic bf16 GEMM (RL-Kernel PR #395, "feat(musa): add native
+ * deterministic gemm kernel", summary: a fixed ascending K-order reduction
+ * with fp32 accumulation; [M, K] @ [N, K]^T without materialising the
+ * transposed right-hand side; dA; the [N, K] weight gradient).
+ *
+ * Every output element is one fp32 accumulation over the contraction index
+ * in ascending order, started at 0, never split; its bits depend only on the
+ * two vectors it contracts (and, for the accumulating output, on its old
+ * value): the forward's and dA's rows do not depend on M.  Inputs are bf16,
+ * row-major, 16-byte aligned; 8 <= N, K <= 2^20, N % 8 == 0, K % 8 == 0,
+ * 0 <= M <= 2^31 (an operand or output of zero bytes may be NULL).  The
+ * output must not overlap an operand.  Outputs:
+ *   BILOGP_GEMM_OUT_BF16       rounded to bf16 (nearest even)
+ *   BILOGP_GEMM_OUT_F32        fp32
+ *   BILOGP_GEMM_OUT_F32_ACCUM  fp32, out = out + (the fp32 product), one add
+ * Same conventions as above (stream-ordered, no sync, status + message). */
+typedef enum bilogp_gemm_out {
+  BILOGP_GEMM_OUT_BF16 = 0,
+  BILOGP_GEMM_OUT_F32 = 1,
+  BILOGP_GEMM_OUT_F32_ACCUM = 2
+} bilogp_gemm_out;
+
+/* C[M, N] = A[M, K] . B[N, K]^T (reduction over K).  M == 0 is a no-op. */
+bilogp_status bilogp_det_gemm_fwd(const void* a, const void* b, void* c, int64_t M, int64_t N,
+                                  int64_t K, int out_kind, void* stream);
+
+/* dA[M, K] = dC[M, N] . B[N, K] (reduction over N): the input gradient of
+ * the forward.  M == 0 is a no-op. */
+bilogp_status bilogp_det_gemm_da(const void* dc, const void* b, void* da, int64_t M, int64_t N,
+                                 int64_t K, int out_kind, void* stream);
+
+/* dB[N, K] = dC[M, N]^T . A[M, K] (reduction over M, ascending): the weight
+ * gradient in the forward's [N, K] layout.  M == 0 writes zeros (or leaves an
+ * accumulating output unchanged). */
+bilogp_status bilogp_det_gemm_db(const void* a, const void* dc, void* db, int64_t M, int64_t N,
+                                 int64_t K, int out_kind, void* stream);
+
 /* Static description of a status code. */
 const char* bilogp_status_string(int status);
 

@@ -11,6 +11,9 @@ count.  Forward only: inputs that require grad while autograd is enabled are
 rejected (RL-Kernel PR #337, author's annotation on the ``requires_grad``
 check: the backward is outside the first contract, so the path fails closed).
 
+``det_gemm``, ``det_gemm_da``, ``det_gemm_db`` and ``DetLinear`` are the
+deterministic GEMM (forward, input gradient, [N, K] weight gradient).
+
 The C entry points of ``include/bilogp.h`` are available under the same
 names (``bilogp_forward``, ``bilogp_forward_ex``, ``bilogp_workspace_bytes``,
 ...), marshalling torch tensors to device pointers and the current stream.
@@ -36,7 +39,13 @@ from ._binding import (  # noqa: F401
     BILOGP_SPLITS_THROUGHPUT,
     BilogpError,
     LIB_PATH,
+    BILOGP_GEMM_OUT_BF16,
+    BILOGP_GEMM_OUT_F32,
+    BILOGP_GEMM_OUT_F32_ACCUM,
     bilogp_abi_version,
+    bilogp_det_gemm_da,
+    bilogp_det_gemm_db,
+    bilogp_det_gemm_fwd,
     bilogp_forward,
     bilogp_forward_ex,
     bilogp_forward_mode,
@@ -55,7 +64,10 @@ from ._binding import (  # noqa: F401
     load_library,
 )
 
-__all__ = ["forward", "workspace_for", "device_cu_count", "BilogpError", "load_library"]
+from .det_gemm import DetLinear, det_gemm, det_gemm_da, det_gemm_db  # noqa: F401,E402
+
+__all__ = ["forward", "workspace_for", "device_cu_count", "BilogpError", "load_library",
+           "det_gemm", "det_gemm_da", "det_gemm_db", "DetLinear"]
 
 
 _SPLIT_MODES = {"invariant": BILOGP_SPLITS_INVARIANT, "throughput": BILOGP_SPLITS_THROUGHPUT}

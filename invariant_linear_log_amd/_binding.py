@@ -27,6 +27,10 @@ BILOGP_BIAS_NONE = 0
 BILOGP_BIAS_BF16 = 1
 BILOGP_BIAS_F32 = 2
 
+BILOGP_GEMM_OUT_BF16 = 0
+BILOGP_GEMM_OUT_F32 = 1
+BILOGP_GEMM_OUT_F32_ACCUM = 2
+
 BILOGP_SPLITS_INVARIANT = 0
 BILOGP_SPLITS_THROUGHPUT = 1
 BILOGP_MAX_THROUGHPUT_SPLITS = 1024
@@ -56,6 +60,9 @@ SIGNATURES = {
     "bilogp_partials": (ctypes.c_int, [_VP, _VP, _VP, _VP, ctypes.c_int, _I64, _I64, _I64, _VP,
                                        ctypes.c_size_t, _VP]),
     "bilogp_merge": (ctypes.c_int, [_VP, _VP, ctypes.c_size_t, _VP, _VP, _I64, _I64, _VP]),
+    "bilogp_det_gemm_fwd": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64, ctypes.c_int, _VP]),
+    "bilogp_det_gemm_da": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64, ctypes.c_int, _VP]),
+    "bilogp_det_gemm_db": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64, ctypes.c_int, _VP]),
     "bilogp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "bilogp_last_error": (ctypes.c_char_p, []),
 }
@@ -241,4 +248,51 @@ def bilogp_merge(target: torch.Tensor, workspace: torch.Tensor, logp_out: torch.
         st = lib.bilogp_merge(_ptr(target), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _ptr(logp_out),
                               _ptr(lse_out), N, V, _stream_handle(stream, target.device))
+    _check(st)
+
+
+# ---------------------------------------------------------------- det_gemm
+def _gemm_kind(out: torch.Tensor, accumulate: bool) -> int:
+    if out.dtype == torch.bfloat16:
+        if accumulate:
+            raise ValueError("accumulation needs a float32 output")
+        return BILOGP_GEMM_OUT_BF16
+    if out.dtype == torch.float32:
+        return BILOGP_GEMM_OUT_F32_ACCUM if accumulate else BILOGP_GEMM_OUT_F32
+    raise TypeError(f"output must be bfloat16 or float32, got {out.dtype}")
+
+
+def bilogp_det_gemm_fwd(a: torch.Tensor, b: torch.Tensor, c: torch.Tensor,
+                        accumulate: bool = False, stream=None) -> None:
+    """``bilogp_det_gemm_fwd``: c[M, N] (=|+=) a[M, K] . b[N, K]^T."""
+    M, K = a.shape
+    N = b.shape[0]
+    with torch.cuda.device(a.device):
+        st = load_library().bilogp_det_gemm_fwd(_ptr(a), _ptr(b), _ptr(c), M, N, K,
+                                                _gemm_kind(c, accumulate),
+                                                _stream_handle(stream, a.device))
+    _check(st)
+
+
+def bilogp_det_gemm_da(dc: torch.Tensor, b: torch.Tensor, da: torch.Tensor,
+                       accumulate: bool = False, stream=None) -> None:
+    """``bilogp_det_gemm_da``: da[M, K] (=|+=) dc[M, N] . b[N, K]."""
+    M, N = dc.shape
+    K = b.shape[1]
+    with torch.cuda.device(dc.device):
+        st = load_library().bilogp_det_gemm_da(_ptr(dc), _ptr(b), _ptr(da), M, N, K,
+                                               _gemm_kind(da, accumulate),
+                                               _stream_handle(stream, dc.device))
+    _check(st)
+
+
+def bilogp_det_gemm_db(a: torch.Tensor, dc: torch.Tensor, db: torch.Tensor,
+                       accumulate: bool = False, stream=None) -> None:
+    """``bilogp_det_gemm_db``: db[N, K] (=|+=) dc[M, N]^T . a[M, K]."""
+    M, K = a.shape
+    N = dc.shape[1]
+    with torch.cuda.device(a.device):
+        st = load_library().bilogp_det_gemm_db(_ptr(a), _ptr(dc), _ptr(db), M, N, K,
+                                               _gemm_kind(db, accumulate),
+                                               _stream_handle(stream, a.device))
     _check(st)

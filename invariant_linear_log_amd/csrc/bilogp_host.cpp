@@ -397,3 +397,104 @@ bilogp_status bilogp_forward(const void* hidden, const void* weight, const int64
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Deterministic GEMM (RL-Kernel PR #395): forward, dA, dB.
+namespace {
+
+constexpr int64_t kMaxGemmNK = int64_t(1) << 20;
+constexpr int64_t kMaxGemmM = int64_t(1) << 31;
+
+struct GemmCall {
+  const void* x;
+  const void* y;
+  void* out;
+  bool xt, yt;
+  int64_t P, Q, C, ldx, ldy, ldo;
+  int out_kind;
+  size_t x_bytes, y_bytes, out_bytes;
+};
+
+bilogp_status gemm_run(const GemmCall& c, int64_t M, int64_t N, int64_t K, void* stream) {
+  g_last_error.clear();
+  // an operand or output of zero bytes is never touched and may be null
+  if ((!c.x && c.x_bytes) || (!c.y && c.y_bytes) || (!c.out && c.out_bytes))
+    return fail(BILOGP_E_INVALID_ARG, "a required pointer is null");
+  if (M < 0 || M > kMaxGemmM) return fail(BILOGP_E_INVALID_ARG, "M out of range [0, 2^31]");
+  if (N < 8 || N > kMaxGemmNK || K < 8 || K > kMaxGemmNK)
+    return fail(BILOGP_E_INVALID_ARG, "N and K must lie in [8, 2^20]");
+  if (c.out_kind != BILOGP_GEMM_OUT_BF16 && c.out_kind != BILOGP_GEMM_OUT_F32 &&
+      c.out_kind != BILOGP_GEMM_OUT_F32_ACCUM)
+    return fail(BILOGP_E_INVALID_ARG, "unknown output kind");
+  if (N % 8 != 0 || K % 8 != 0) return fail(BILOGP_E_UNSUPPORTED, "N and K must be multiples of 8");
+  if ((reinterpret_cast<uintptr_t>(c.x) | reinterpret_cast<uintptr_t>(c.y) |
+       reinterpret_cast<uintptr_t>(c.out)) % 16)
+    return fail(BILOGP_E_UNSUPPORTED, "operands and output must be 16-byte aligned");
+  if (c.out_bytes == 0) return BILOGP_OK;        // empty output: nothing to write
+  const Range ro = range_of(c.out, c.out_bytes);
+  if (overlap(ro, range_of(c.x, c.x_bytes)) || overlap(ro, range_of(c.y, c.y_bytes)))
+    return fail(BILOGP_E_INVALID_ARG, "the output overlaps an operand");
+  int dev = -1;
+  bilogp_status st = check_device(&dev);
+  if (st != BILOGP_OK) return st;
+  const void* ptrs[] = {c.x_bytes ? c.x : nullptr, c.y_bytes ? c.y : nullptr, c.out};
+  const char* names[] = {"operand", "operand", "output"};
+  for (int i = 0; i < 3; ++i) {
+    if (!ptrs[i]) continue;
+    st = check_on_device(ptrs[i], dev, names[i]);
+    if (st != BILOGP_OK) return st;
+  }
+  bilogp::GemmParams g;
+  g.x = c.x;
+  g.y = c.y;
+  g.out = c.out;
+  g.P = c.P;
+  g.Q = c.Q;
+  g.C = c.C;
+  g.ldx = c.ldx;
+  g.ldy = c.ldy;
+  g.ldo = c.ldo;
+  g.out_kind = c.out_kind;
+  g.Pt = (int32_t)((c.P + 255) / 256);
+  g.Qt = (int32_t)((c.Q + 255) / 256);
+  if ((int64_t)g.Pt * g.Qt > INT32_MAX) return fail(BILOGP_E_INVALID_ARG, "too many tiles");
+  hipError_t e = bilogp::launch_det_gemm(g, c.xt, c.yt, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(BILOGP_E_HIP, std::string("gemm launch: ") + hipGetErrorString(e));
+  return BILOGP_OK;
+}
+
+size_t out_elem(int kind) { return kind == BILOGP_GEMM_OUT_BF16 ? 2 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+bilogp_status bilogp_det_gemm_fwd(const void* a, const void* b, void* c, int64_t M, int64_t N,
+                                  int64_t K, int out_kind, void* stream) {
+  // C[M, N] = A[M, K] . B[N, K]^T: p = n (X = B), q = m (Y = A), contraction k
+  const GemmCall g{b, a, c, false, false, N, M, K, K, K, N, out_kind,
+                   (size_t)N * K * 2, (size_t)(M > 0 ? M : 0) * K * 2,
+                   (size_t)(M > 0 ? M : 0) * N * out_elem(out_kind)};
+  return gemm_run(g, M, N, K, stream);
+}
+
+bilogp_status bilogp_det_gemm_da(const void* dc, const void* b, void* da, int64_t M, int64_t N,
+                                 int64_t K, int out_kind, void* stream) {
+  // dA[M, K] = dC[M, N] . B[N, K]: p = k (X = B, stored [n][k]), q = m (Y = dC)
+  const GemmCall g{b, dc, da, true, false, K, M, N, K, N, K, out_kind,
+                   (size_t)N * K * 2, (size_t)(M > 0 ? M : 0) * N * 2,
+                   (size_t)(M > 0 ? M : 0) * K * out_elem(out_kind)};
+  return gemm_run(g, M, N, K, stream);
+}
+
+bilogp_status bilogp_det_gemm_db(const void* a, const void* dc, void* db, int64_t M, int64_t N,
+                                 int64_t K, int out_kind, void* stream) {
+  // dB[N, K] = dC[M, N]^T . A[M, K]: p = k (X = A, stored [m][k]), q = n (Y = dC,
+  // stored [m][n]), contraction m
+  const GemmCall g{a, dc, db, true, true, K, N, M, K, N, K, out_kind,
+                   (size_t)(M > 0 ? M : 0) * K * 2, (size_t)(M > 0 ? M : 0) * N * 2,
+                   (size_t)N * K * out_elem(out_kind)};
+  return gemm_run(g, M, N, K, stream);
+}
+
+}  // extern "C"

@@ -50,4 +50,23 @@ hipError_t launch_merge(const float2* part, const float* tlogit, const int64_t* 
                         float* logp, float* lse, int64_t N, int32_t S, int32_t V,
                         hipStream_t stream);
 
+// Deterministic GEMM: D[p, q] = sum_c X[p, c] * Y[q, c] over ascending c,
+// fp32 accumulation, written as out[q][p].  An operand is read either from
+// its natural layout (X[p][c] at x + p * ldx + c: contraction contiguous) or
+// transposed (stored as [c][p] at x + c * ldx + p).
+struct GemmParams {
+  const void* x;           // bf16
+  const void* y;           // bf16
+  void* out;               // out[q][p] at out + q * ldo + p: fp32 or bf16
+  int64_t P, Q, C;
+  int64_t ldx, ldy, ldo;   // row pitches in elements
+  int32_t out_kind;        // GemmOut
+  int32_t Pt, Qt;          // 256-wide tiles along P and Q
+};
+
+enum GemmOut : int32_t { kGemmBf16 = 0, kGemmF32 = 1, kGemmF32Accum = 2 };
+
+// Enqueue the GEMM; x_t / y_t select the transposed storage of X / Y.
+hipError_t launch_det_gemm(const GemmParams& g, bool x_t, bool y_t, hipStream_t stream);
+
 }  // namespace bilogp

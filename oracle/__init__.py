@@ -20,6 +20,13 @@ linear_logp
     ``split_merge_linear_logp``   the method's own steps: per-split online
                                   (max, sum-exp) partials, then the ascending combine
     ``brute_force_linear_logp``   pure-Python ``math.fsum`` version for tiny inputs
+
+det_gemm (RL-Kernel PR #395, "feat(musa): add native deterministic gemm kernel")
+    ``det_gemm_fwd``              C = A . B^T, float64
+    ``det_gemm_da``               dA = dC . B, float64
+    ``det_gemm_db``               dB = dC^T . A ([N, K] weight-gradient layout), float64
+    ``abs_product``               sums of |terms|: the fp32 rounding-error scale
+    ``brute_force_fwd``           pure-Python ``math.fsum`` forward for tiny inputs
 """
 
 from .linear_logp import (  # noqa: F401
@@ -30,4 +37,11 @@ from .linear_logp import (  # noqa: F401
     vocab_splits_throughput,
     split_merge_linear_logp,
     brute_force_linear_logp,
+)
+from .det_gemm import (  # noqa: F401
+    det_gemm_fwd,
+    det_gemm_da,
+    det_gemm_db,
+    abs_product,
+    brute_force_fwd,
 )

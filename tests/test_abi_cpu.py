@@ -253,3 +253,59 @@ def test_binding_raises_when_library_missing(tmp_path):
             B.load_library(str(tmp_path / "libbilogp.so"))
     finally:
         B._lib = saved
+
+
+# ------------------------------------------------------------- det_gemm checks
+def _gemm(fn="bilogp_det_gemm_fwd", x=FAKE, y=FAKE + 0x1000000, out=FAKE + 0x2000000, M=64,
+          N=64, K=64, kind=0):
+    return getattr(ila.load_library(), fn)(x, y, out, M, N, K, kind, None)
+
+
+@pytest.mark.parametrize("fn", ["bilogp_det_gemm_fwd", "bilogp_det_gemm_da",
+                                "bilogp_det_gemm_db"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), B.BILOGP_E_INVALID_ARG),
+    (dict(y=None), B.BILOGP_E_INVALID_ARG),
+    (dict(out=None), B.BILOGP_E_INVALID_ARG),
+    (dict(M=-1), B.BILOGP_E_INVALID_ARG),
+    (dict(N=0), B.BILOGP_E_INVALID_ARG),
+    (dict(K=4), B.BILOGP_E_INVALID_ARG),
+    (dict(N=(1 << 20) + 8), B.BILOGP_E_INVALID_ARG),
+    (dict(kind=3), B.BILOGP_E_INVALID_ARG),
+    (dict(N=60), B.BILOGP_E_UNSUPPORTED),          # N % 8 != 0
+    (dict(K=68 + 2), B.BILOGP_E_UNSUPPORTED),      # K % 8 != 0
+    (dict(x=FAKE + 8), B.BILOGP_E_UNSUPPORTED),    # misaligned
+    (dict(out=FAKE + 0x2000004), B.BILOGP_E_UNSUPPORTED),
+    (dict(out=FAKE), B.BILOGP_E_INVALID_ARG),      # output aliases an operand
+])
+def test_det_gemm_fails_closed(fn, kw, status):
+    st = _gemm(fn, **kw)
+    assert st == status, (fn, kw, st, ila.bilogp_last_error())
+    assert ila.bilogp_last_error() != ""
+
+
+def test_det_gemm_empty_batch():
+    # forward and dA with M == 0 write nothing and succeed without a device
+    assert _gemm("bilogp_det_gemm_fwd", M=0) == B.BILOGP_OK
+    assert _gemm("bilogp_det_gemm_da", M=0) == B.BILOGP_OK
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU path")
+def test_det_gemm_no_device_is_unsupported():
+    assert _gemm() == B.BILOGP_E_UNSUPPORTED
+    # dB with M == 0 still writes its (zero) [N, K] output: it needs the device
+    assert _gemm("bilogp_det_gemm_db", M=0) == B.BILOGP_E_UNSUPPORTED
+
+
+def test_det_gemm_wrappers_reject_bad_inputs():
+    a = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        ila.det_gemm(a.float(), a)
+    with pytest.raises(ValueError):
+        ila.det_gemm(a, torch.zeros(4, 16, dtype=torch.bfloat16))      # K mismatch
+    with pytest.raises(ValueError):
+        ila.det_gemm(a, a)                                              # not on a GPU
+    with pytest.raises(ValueError):
+        ila.det_gemm_da(torch.zeros(4, 3, dtype=torch.bfloat16), a)     # N mismatch
+    with pytest.raises(ValueError):
+        ila.det_gemm_db(a, torch.zeros(5, 8, dtype=torch.bfloat16))     # M mismatch
