@@ -27,6 +27,12 @@ det_gemm (RL-Kernel PR #395, "feat(musa): add native deterministic gemm kernel")
     ``det_gemm_db``               dB = dC^T . A ([N, K] weight-gradient layout), float64
     ``abs_product``               sums of |terms|: the fp32 rounding-error scale
     ``brute_force_fwd``           pure-Python ``math.fsum`` forward for tiny inputs
+
+linear_logp_grad (the backward: derivatives of PR #337's forward, in PR #395's layouts)
+    ``softmax_grad``              dZ = g_lse P + g_logp (onehot - P), float64
+    ``linear_logp_backward``      (grad_hidden, grad_weight, grad_bias), float64
+    ``grad_hidden_rows``          grad_hidden for a subset of rows
+    ``grad_weight_rows``          (grad_weight, grad_bias) for a subset of vocabulary rows
 """
 
 from .linear_logp import (  # noqa: F401
@@ -44,4 +50,10 @@ from .det_gemm import (  # noqa: F401
     det_gemm_db,
     abs_product,
     brute_force_fwd,
+)
+from .linear_logp_grad import (  # noqa: F401
+    softmax_grad,
+    linear_logp_backward,
+    grad_hidden_rows,
+    grad_weight_rows,
 )

@@ -40,7 +40,8 @@ from typing import Dict, Optional
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_custom", "peaky_argmax_rows"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_custom", "make_upstream_grads",
+           "peaky_argmax_rows"]
 
 
 @dataclass(frozen=True)
@@ -182,6 +183,18 @@ def make_custom(N: int, H: int, V: int, seed: int, w_std: Optional[float] = None
     dev = torch.device(device)
     return {"hidden": hidden.to(dev), "weight": weight.to(dev), "target": target.to(dev),
             "bias": None if b is None else b.to(dev)}
+
+
+def make_upstream_grads(N: int, seed: int, g_lse_std: float = 0.1, device="cpu") -> dict:
+    """Upstream gradients of the forward's two outputs for the backward:
+    ``grad_logp`` ~ N(0, 1) (a per-token policy-gradient weight) and
+    ``grad_lse`` ~ N(0, g_lse_std^2) (a small log-partition penalty), fp32 [N],
+    drawn on the CPU, then moved."""
+    gen = torch.Generator().manual_seed(seed)
+    g_logp = torch.randn((N,), generator=gen, dtype=torch.float32)
+    g_lse = torch.randn((N,), generator=gen, dtype=torch.float32).mul_(g_lse_std)
+    dev = torch.device(device)
+    return {"grad_logp": g_logp.to(dev), "grad_lse": g_lse.to(dev)}
 
 
 def peaky_argmax_rows(inputs: dict) -> torch.Tensor:
