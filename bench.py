@@ -3,7 +3,8 @@
 one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--no-backward] [--no-det-gemm]
+                    [--no-invariance-cost]
 
 One step is one full pass of the hot path over one batch: bilogp_partials
 (fused bf16-MFMA projection + per-split online softmax) followed by
@@ -38,7 +39,7 @@ PEAK_HBM_GBPS = 8000.0
 # reads for a plain 1 GiB device copy (x2.000 and x1.000).  Keyed by the sha256 prefix
 # of the kernel source the counters were taken on: any other source reports null.
 MEASURED_TRAFFIC = {
-    ("headline", "c3c05705a3550113"): {"fetch_bytes": 6619886587, "write_bytes": 3149016},
+    ("headline", "5c4238012b0f3a2f"): {"fetch_bytes": 6619391894, "write_bytes": 3103856},
 }
 
 
@@ -51,6 +52,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-det-gemm", action="store_true",
                     help="skip timing the deterministic GEMM (forward, dA, dB)")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip timing the deterministic backward")
     ap.add_argument("--no-invariance-cost", action="store_true",
                     help="skip timing the throughput split policy beside the invariant one")
     ap.add_argument("--cpu-rows", type=int, default=4096,
@@ -157,6 +160,43 @@ def det_gemm_leg(steps=10, warmup=3):
         rec["fwd"]["frac"] = rec["fwd"]["tflops"] / PEAK_BF16_TFLOPS
         out[f"M{M}_N{N}_K{K}"] = rec
     return out
+
+
+def backward_leg(h, t, w, b, lse, steps=10, warmup=3):
+    """The deterministic backward (bilogp_backward: softmax-gradient
+    projection kernel, grad_hidden and grad_weight GEMMs, bias row sums) on
+    the workload's own shapes with seeded upstream gradients; 6 N H V flops
+    per call (z recomputed, then two products of the same size)."""
+    import torch
+    import invariant_linear_log_amd as ila
+    import synth
+    dev = h.device
+    N, H = h.shape
+    V = w.shape[0]
+    up = synth.make_upstream_grads(N, 12, device=dev)
+    gh = torch.empty((N, H), dtype=torch.float32, device=dev)
+    gw = torch.empty((V, H), dtype=torch.float32, device=dev)
+    gb = None if b is None else torch.empty(V, dtype=torch.float32, device=dev)
+    ws = ila.backward_workspace_for(N, V, dev)
+    stream = torch.cuda.Stream(device=dev)
+
+    def run():
+        ila.bilogp_backward(h, w, t, b, lse, up["grad_logp"], up["grad_lse"], gh, gw, gb, ws,
+                            stream=stream)
+    for _ in range(warmup):
+        run()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 6.0 * N * H * V
+    return {"ms": ms, "tflops": flops / ms / 1e9, "frac": flops / ms / 1e9 / PEAK_BF16_TFLOPS,
+            "tokens_per_s": N / ms * 1e3, "flops": flops,
+            "finite": bool(torch.isfinite(gh).all()) and bool(torch.isfinite(gw).all())}
 
 
 def cpu_baseline(inp, rows_n, seed=7):
@@ -277,6 +317,8 @@ def main():
     }
     if not args.no_invariance_cost:
         out["invariance_cost"] = invariance_cost(h, t, w, b)
+    if not args.no_backward:
+        out["backward"] = backward_leg(h, t, w, b, lse)
     if not args.no_det_gemm:
         out["det_gemm"] = det_gemm_leg()
     if not args.no_cpu_baseline:

@@ -19,8 +19,10 @@
  * V: never on N, on the position of the row in the batch, on the other rows,
  * or on the number of compute units.
  *
- * Forward only.  The page's first contract excludes the backward; the entry
- * points take no gradient state.
+ * The page's first contract is forward-only (author's annotation on the
+ * requires_grad check: the backward lies outside it).  bilogp_backward, at
+ * the end of this header, extends it with a deterministic backward built on
+ * the same projection tiles and on the deterministic GEMM below.
  *
  * Conventions for every entry point
  *  - Ownership: the caller owns every buffer.  The library keeps no device
@@ -225,6 +227,58 @@ bilogp_status bilogp_det_gemm_da(const void* dc, const void* b, void* da, int64_
  * accumulating output unchanged). */
 bilogp_status bilogp_det_gemm_db(const void* a, const void* dc, void* db, int64_t M, int64_t N,
                                  int64_t K, int out_kind, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Deterministic backward of the fused linear log-probability.
+ *
+ * The first contract of RL-Kernel PR #337 stops at the forward (author's
+ * annotation on the requires_grad check); this extends it with the gradients
+ * of the forward's two outputs, reduced in fixed orders with the
+ * deterministic GEMM of RL-Kernel PR #395 (summary: dA = dC . B and the
+ * weight gradient in the forward's [V, H] layout, fixed ascending
+ * contraction, fp32 accumulation).  With P[i, v] = exp(z[i, v] - lse[i])
+ * and the upstream gradients g_logp[i] (of logp[i]) and g_lse[i] (of
+ * lse[i]):
+ *
+ *     dZ[i, v]       = g_lse[i] P[i, v] + g_logp[i] ([v == target[i]] - P[i, v])
+ *     grad_hidden    = dZ . W            [N, H], reduction over v ascending
+ *     grad_weight    = dZ^T . hidden     [V, H], reduction over i ascending
+ *     grad_bias[v]   = sum_i dZ[i, v]    [V],    i ascending, fixed tree
+ *
+ * (g_logp = -1, g_lse = 0 is the cross-entropy gradient softmax - onehot.)
+ * z is recomputed tile by tile exactly as the forward computes it; dZ is
+ * rounded to bf16 (nearest even), the operand type of the two products, and
+ * stored transposed in the workspace ([V, ldz] with ldz = N rounded up to 8);
+ * the [N, V] logits are never stored in fp32.  A target outside [0, V)
+ * contributes no one-hot term.
+ *
+ * Bit contract: row i of grad_hidden depends only on hidden[i], target[i],
+ * lse[i], g_logp[i], g_lse[i], W, bias, H and V - not on N or on the other
+ * rows.  grad_weight and grad_bias sum over the batch in ascending row
+ * order: the same bits on every run, stream and device.
+ *
+ *   hidden, weight, target, bias, bias_dtype   as for bilogp_forward_ex
+ *   lse          device, fp32 [N]: the forward's lse for these inputs
+ *   grad_logp    device, fp32 [N]
+ *   grad_lse     device, fp32 [N]
+ *   grad_hidden  device, fp32 [N, H] (written), 16-byte aligned
+ *   grad_weight  device, fp32 [V, H] (written), 16-byte aligned
+ *   grad_bias    device, fp32 [V] (written), or NULL for no bias gradient
+ *   workspace    device, at least bilogp_backward_workspace_bytes(N, V)
+ *                bytes, 256-byte aligned; holds dZ^T between the kernels
+ *   0 <= N <= 2^21 (N == 0 writes zeros to grad_weight and grad_bias; the
+ *   [N] inputs and grad_hidden may then be NULL), H and V as for the
+ *   forward.  The gradients must not overlap each other, an input or the
+ *   workspace.  Same conventions as above (stream-ordered, no sync, status +
+ *   message, nothing launched on an error).
+ */
+size_t bilogp_backward_workspace_bytes(int64_t N, int64_t V);
+
+bilogp_status bilogp_backward(const void* hidden, const void* weight, const int64_t* target,
+                              const void* bias, int bias_dtype, const float* lse,
+                              const float* grad_logp, const float* grad_lse, float* grad_hidden,
+                              float* grad_weight, float* grad_bias, int64_t N, int64_t H,
+                              int64_t V, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* bilogp_status_string(int status);

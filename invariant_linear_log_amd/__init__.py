@@ -13,6 +13,9 @@ check: the backward is outside the first contract, so the path fails closed).
 
 ``det_gemm``, ``det_gemm_da``, ``det_gemm_db`` and ``DetLinear`` are the
 deterministic GEMM (forward, input gradient, [N, K] weight gradient).
+``backward`` and the autograd-capable ``linear_logp`` add a deterministic
+backward to the forward (gradients of logp and lse with respect to hidden,
+weight and bias).
 
 The C entry points of ``include/bilogp.h`` are available under the same
 names (``bilogp_forward``, ``bilogp_forward_ex``, ``bilogp_workspace_bytes``,
@@ -43,6 +46,8 @@ from ._binding import (  # noqa: F401
     BILOGP_GEMM_OUT_F32,
     BILOGP_GEMM_OUT_F32_ACCUM,
     bilogp_abi_version,
+    bilogp_backward,
+    bilogp_backward_workspace_bytes,
     bilogp_det_gemm_da,
     bilogp_det_gemm_db,
     bilogp_det_gemm_fwd,
@@ -65,9 +70,11 @@ from ._binding import (  # noqa: F401
 )
 
 from .det_gemm import DetLinear, det_gemm, det_gemm_da, det_gemm_db  # noqa: F401,E402
+from .grad import LinearLogp, backward, backward_workspace_for, linear_logp  # noqa: F401,E402
 
 __all__ = ["forward", "workspace_for", "device_cu_count", "BilogpError", "load_library",
-           "det_gemm", "det_gemm_da", "det_gemm_db", "DetLinear"]
+           "det_gemm", "det_gemm_da", "det_gemm_db", "DetLinear", "backward",
+           "backward_workspace_for", "linear_logp", "LinearLogp"]
 
 
 _SPLIT_MODES = {"invariant": BILOGP_SPLITS_INVARIANT, "throughput": BILOGP_SPLITS_THROUGHPUT}

@@ -63,6 +63,9 @@ SIGNATURES = {
     "bilogp_det_gemm_fwd": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64, ctypes.c_int, _VP]),
     "bilogp_det_gemm_da": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64, ctypes.c_int, _VP]),
     "bilogp_det_gemm_db": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64, ctypes.c_int, _VP]),
+    "bilogp_backward_workspace_bytes": (ctypes.c_size_t, [_I64, _I64]),
+    "bilogp_backward": (ctypes.c_int, [_VP, _VP, _VP, _VP, ctypes.c_int, _VP, _VP, _VP, _VP, _VP,
+                                       _VP, _I64, _I64, _I64, _VP, ctypes.c_size_t, _VP]),
     "bilogp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "bilogp_last_error": (ctypes.c_char_p, []),
 }
@@ -295,4 +298,31 @@ def bilogp_det_gemm_db(a: torch.Tensor, dc: torch.Tensor, db: torch.Tensor,
         st = load_library().bilogp_det_gemm_db(_ptr(a), _ptr(dc), _ptr(db), M, N, K,
                                                _gemm_kind(db, accumulate),
                                                _stream_handle(stream, a.device))
+    _check(st)
+
+
+# ---------------------------------------------------------------- backward
+def bilogp_backward_workspace_bytes(N: int, V: int) -> int:
+    return load_library().bilogp_backward_workspace_bytes(N, V)
+
+
+def bilogp_backward(hidden: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
+                    bias: Optional[torch.Tensor], lse: torch.Tensor, grad_logp: torch.Tensor,
+                    grad_lse: torch.Tensor, grad_hidden: torch.Tensor,
+                    grad_weight: torch.Tensor, grad_bias: Optional[torch.Tensor],
+                    workspace: torch.Tensor, stream=None) -> None:
+    """``bilogp_backward`` on 2-D contiguous device tensors: hidden [N, H] and
+    weight [V, H] bf16, target [N] int64, bias [V] or None, lse / grad_logp /
+    grad_lse [N] fp32; writes grad_hidden [N, H], grad_weight [V, H] and
+    grad_bias [V] (fp32, grad_bias optional)."""
+    N, H = hidden.shape
+    V = weight.shape[0]
+    ws_bytes = workspace.numel() * workspace.element_size()
+    lib = load_library()
+    with torch.cuda.device(weight.device):
+        st = lib.bilogp_backward(_ptr(hidden), _ptr(weight), _ptr(target), _ptr(bias),
+                                 _bias_dtype(bias), _ptr(lse), _ptr(grad_logp), _ptr(grad_lse),
+                                 _ptr(grad_hidden), _ptr(grad_weight), _ptr(grad_bias), N, H, V,
+                                 _ptr(workspace), ws_bytes,
+                                 _stream_handle(stream, weight.device))
     _check(st)

@@ -498,3 +498,142 @@ bilogp_status bilogp_det_gemm_db(const void* a, const void* dc, void* db, int64_
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Backward of the fused linear log-probability (row f2).
+namespace {
+
+constexpr int64_t kMaxBwdN = int64_t(1) << 21;
+
+int64_t dz_ld(int64_t N) { return (N + 7) / 8 * 8; }
+
+}  // namespace
+
+extern "C" {
+
+size_t bilogp_backward_workspace_bytes(int64_t N, int64_t V) {
+  if (N < 0 || N > kMaxBwdN || V <= 0 || V > kMaxV) return (size_t)-1;
+  return round_up((size_t)V * (size_t)dz_ld(N) * 2) + round_up(padded_vocab(V) * sizeof(float));
+}
+
+bilogp_status bilogp_backward(const void* hidden, const void* weight, const int64_t* target,
+                              const void* bias, int bias_dtype, const float* lse,
+                              const float* grad_logp, const float* grad_lse, float* grad_hidden,
+                              float* grad_weight, float* grad_bias, int64_t N, int64_t H,
+                              int64_t V, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!weight || !grad_weight || (N > 0 && (!hidden || !target || !lse || !grad_logp ||
+                                            !grad_lse || !grad_hidden)))
+    return fail(BILOGP_E_INVALID_ARG, "a required pointer is null");
+  if (N < 0 || N > kMaxBwdN) return fail(BILOGP_E_INVALID_ARG, "N out of range [0, 2^21]");
+  if (H <= 0 || H > kMaxH) return fail(BILOGP_E_INVALID_ARG, "H out of range [1, 2^20]");
+  if (V <= 0 || V > kMaxV) return fail(BILOGP_E_INVALID_ARG, "V out of range [1, 2^30]");
+  if (bias_dtype != BILOGP_BIAS_NONE && bias_dtype != BILOGP_BIAS_BF16 &&
+      bias_dtype != BILOGP_BIAS_F32)
+    return fail(BILOGP_E_UNSUPPORTED, "unknown bias dtype");
+  if ((bias_dtype == BILOGP_BIAS_NONE) != (bias == nullptr))
+    return fail(BILOGP_E_INVALID_ARG, "bias must be null exactly when bias_dtype is NONE");
+  if (H % 8 != 0) return fail(BILOGP_E_UNSUPPORTED, "H must be a multiple of 8");
+  if ((reinterpret_cast<uintptr_t>(hidden) | reinterpret_cast<uintptr_t>(weight) |
+       reinterpret_cast<uintptr_t>(grad_hidden) | reinterpret_cast<uintptr_t>(grad_weight)) % 16)
+    return fail(BILOGP_E_UNSUPPORTED, "hidden, weight and the gradients must be 16-byte aligned");
+  const size_t bias_esz = bias_dtype == BILOGP_BIAS_F32 ? 4 : 2;
+  if (bias && reinterpret_cast<uintptr_t>(bias) % bias_esz != 0)
+    return fail(BILOGP_E_UNSUPPORTED, "bias is misaligned for its dtype");
+  if ((reinterpret_cast<uintptr_t>(target) % 8) ||
+      ((reinterpret_cast<uintptr_t>(lse) | reinterpret_cast<uintptr_t>(grad_logp) |
+        reinterpret_cast<uintptr_t>(grad_lse) | reinterpret_cast<uintptr_t>(grad_bias)) % 4))
+    return fail(BILOGP_E_UNSUPPORTED, "target, lse, grad_logp, grad_lse or grad_bias misaligned");
+  const size_t need = bilogp_backward_workspace_bytes(N, V);
+  if (!workspace || workspace_bytes < need)
+    return fail(BILOGP_E_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+    return fail(BILOGP_E_WORKSPACE, "workspace must be 256-byte aligned");
+  // outputs must not overlap each other, the inputs or the workspace
+  const Range outs[] = {range_of(grad_hidden, (size_t)N * H * 4),
+                        range_of(grad_weight, (size_t)V * H * 4),
+                        grad_bias ? range_of(grad_bias, (size_t)V * 4) : Range{0, 0}};
+  const Range ins[] = {range_of(hidden, (size_t)N * H * 2), range_of(weight, (size_t)V * H * 2),
+                       range_of(target, (size_t)N * 8),
+                       bias ? range_of(bias, (size_t)V * bias_esz) : Range{0, 0},
+                       range_of(lse, (size_t)N * 4), range_of(grad_logp, (size_t)N * 4),
+                       range_of(grad_lse, (size_t)N * 4), range_of(workspace, workspace_bytes)};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return fail(BILOGP_E_INVALID_ARG, "gradients overlap");
+    for (const Range& in : ins)
+      if (overlap(outs[i], in))
+        return fail(BILOGP_E_INVALID_ARG, "a gradient overlaps an input or the workspace");
+  }
+
+  int dev = -1;
+  bilogp_status st = check_device(&dev);
+  if (st != BILOGP_OK) return st;
+  const void* ptrs[] = {hidden, weight, target, bias, lse, grad_logp, grad_lse, grad_hidden,
+                        grad_weight, grad_bias, workspace};
+  for (const void* q : ptrs) {
+    if (!q) continue;
+    st = check_on_device(q, dev, "an argument");
+    if (st != BILOGP_OK) return st;
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t ldz = dz_ld(N);
+  uint16_t* dzt = static_cast<uint16_t*>(workspace);
+  float* bias32 = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                           round_up((size_t)V * (size_t)ldz * 2));
+  const int32_t kind = bias_dtype == BILOGP_BIAS_BF16 ? bilogp::kBiasBf16
+                       : bias_dtype == BILOGP_BIAS_F32 ? bilogp::kBiasF32
+                                                       : bilogp::kBiasNone;
+  hipError_t e = hipSuccess;
+  if (N > 0) {
+    if (bias) e = bilogp::launch_bias_f32(bias, kind, (int32_t)V, bias32, s);
+    if (e == hipSuccess) e = bilogp::launch_zero_pad_cols(dzt, V, N, ldz, s);
+    if (e == hipSuccess) {
+      bilogp::ProjParams p{};
+      p.hidden = hidden;
+      p.weight = weight;
+      p.target = target;
+      p.bias = bias ? bias32 : nullptr;
+      p.N = N;
+      p.H = (int32_t)H;
+      p.V = (int32_t)V;
+      p.bias_kind = kind;
+      p.T = (int32_t)((V + bilogp::kVtileCols - 1) / bilogp::kVtileCols);
+      p.vps = bilogp_vtiles_per_split(V);
+      p.S = bilogp_num_vocab_splits(V);
+      p.R = (int32_t)((N + bilogp::kBlockRows - 1) / bilogp::kBlockRows);
+      p.lse = lse;
+      p.g_logp = grad_logp;
+      p.g_lse = grad_lse;
+      p.dzt = dzt;
+      p.ldz = ldz;
+      e = bilogp::launch_softmax_grad(p, s);
+    }
+    if (e == hipSuccess) {
+      // grad_hidden[n][h] = sum over v ascending of dZ^T[v][n] W[v][h]
+      bilogp::GemmParams g{};
+      g.x = weight; g.y = dzt; g.out = grad_hidden;
+      g.P = H; g.Q = N; g.C = V; g.ldx = H; g.ldy = ldz; g.ldo = H;
+      g.out_kind = bilogp::kGemmF32;
+      g.Pt = (int32_t)((H + 255) / 256);
+      g.Qt = (int32_t)((N + 255) / 256);
+      e = bilogp::launch_det_gemm(g, true, true, s);
+    }
+  }
+  if (e == hipSuccess) {
+    // grad_W[v][h] = sum over n ascending of dZ^T[v][n] hidden[n][h] (zero if N == 0)
+    bilogp::GemmParams g{};
+    g.x = hidden; g.y = dzt; g.out = grad_weight;
+    g.P = H; g.Q = V; g.C = N; g.ldx = H; g.ldy = ldz; g.ldo = H;
+    g.out_kind = bilogp::kGemmF32;
+    g.Pt = (int32_t)((H + 255) / 256);
+    g.Qt = (int32_t)((V + 255) / 256);
+    e = bilogp::launch_det_gemm(g, true, false, s);
+  }
+  if (e == hipSuccess && grad_bias) e = bilogp::launch_row_sums(dzt, V, N, ldz, grad_bias, s);
+  if (e != hipSuccess) return fail(BILOGP_E_HIP, std::string("backward launch: ") + hipGetErrorString(e));
+  return BILOGP_OK;
+}
+
+}  // extern "C"

@@ -35,6 +35,13 @@ struct ProjParams {
   int32_t vps;             // tiles per split
   int32_t S;               // splits
   int32_t R;               // row blocks, ceil(N / kBlockRows)
+  // backward only (softmax-gradient kernel): the forward's lse, the upstream
+  // gradients of logp and lse, and dZ^T [V, ldz] (bf16) written per tile
+  const float* lse;
+  const float* g_logp;
+  const float* g_lse;
+  uint16_t* dzt;
+  int64_t ldz;
 };
 
 // Enqueue the exact fp32 copy of a bf16 / fp32 bias, zero-padded to whole
@@ -44,6 +51,19 @@ hipError_t launch_bias_f32(const void* bias, int32_t kind, int32_t V, float* out
 
 // Enqueue the fused projection + per-split online-softmax kernel.
 hipError_t launch_proj_lse(const ProjParams& p, hipStream_t stream);
+
+// Enqueue the softmax-gradient kernel: the same projection tiles, and per
+// logit dZ = p (g_lse - g_logp) + g_logp [v == target], p = exp(z - lse),
+// stored to dZ^T as bf16 (columns of p.dzt past N untouched).
+hipError_t launch_softmax_grad(const ProjParams& p, hipStream_t stream);
+
+// Enqueue dZ^T padding: zero columns [N, ldz) of every row of dZ^T.
+hipError_t launch_zero_pad_cols(uint16_t* dzt, int64_t rows, int64_t N, int64_t ldz,
+                                hipStream_t stream);
+
+// Enqueue grad_bias[v] = sum over n ascending of dZ^T[v][n] (fp32 out).
+hipError_t launch_row_sums(const uint16_t* dzt, int64_t rows, int64_t N, int64_t ldz,
+                           float* out, hipStream_t stream);
 
 // Enqueue the ascending split merge: lse and logp per row.
 hipError_t launch_merge(const float2* part, const float* tlogit, const int64_t* target,

@@ -120,9 +120,17 @@ __device__ __forceinline__ void merge_state(float m_lo, float s_lo, float m_hi, 
 template <int I>
 using Slot = std::integral_constant<int, I>;
 
-// The kernel body, instantiated once with bias and once without (two plain
-// kernels below), so the bias-free path carries no bias code.
-template <bool kHasBias>
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// The kernel body, instantiated with and without bias, and (kGrad) as the
+// softmax-gradient pass of the backward: the same tiles and the same
+// accumulation, with an epilogue that writes dZ instead of reducing it.
+template <bool kHasBias, bool kGrad>
 __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
   // Two LDS buffers, each its own variable, so the compiler can tell a read
   // of one from a direct-to-LDS load into the other and does not drain the
@@ -205,6 +213,21 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
   for (int ti = 0; ti < 2; ++ti) {
     const int j = wt * 64 + ti * 32 + (lane & 31);
     tgt[ti] = (j < rows_here) ? p.target[m0 + j] : (int64_t)-1;
+  }
+  // backward: the forward's lse and the coefficients of
+  // dZ = p (g_lse - g_logp) + g_logp [v == target] for the lane's two rows
+  float g_lse_row[2] = {0.f, 0.f}, g_coef[2] = {0.f, 0.f}, g_tgt[2] = {0.f, 0.f};
+  if constexpr (kGrad) {
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) {
+      const int j = wt * 64 + ti * 32 + (lane & 31);
+      if (j < rows_here) {
+        const float gl = p.g_logp[m0 + j];
+        g_lse_row[ti] = p.lse[m0 + j];
+        g_coef[ti] = p.g_lse[m0 + j] - gl;
+        g_tgt[ti] = gl;
+      }
+    }
   }
 
   // Direct-to-LDS loads of stage g into buffer SC, one instruction at a
@@ -371,6 +394,40 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
     // vocabulary row wv*128 + vi*32 + 8*(r/4) + 4*half + (r%4) of the tile.
     const int vbase = (vt_begin + v) * kVtileCols;
     const int vw = vbase + wv * 128;               // first column of this wave
+    if constexpr (kGrad) {
+      // dZ^T[col][row] = p (g_lse - g_logp) + g_logp [col == target], p =
+      // exp(z - lse): 32 consecutive rows per store (coalesced).  The buffer
+      // covers the tile's columns below V, so stores past V are dropped.
+      const int vrows = min(kVtileCols, p.V - vbase);
+      const __amdgpu_buffer_rsrc_t rs_dz = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.dzt + (int64_t)vbase * p.ldz), (short)0, vrows * (int)p.ldz * 2, kRsrcWord3);
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti) {
+        const int jr = wt * 64 + ti * 32 + (lane & 31);
+        if (jr >= rows_here) continue;
+        uint32_t vo = ((uint32_t)(wv * 128 + 4 * half) * (uint32_t)p.ldz + (uint32_t)(m0 + jr)) * 2u;
+        uint32_t ld2 = (uint32_t)p.ldz * 2u;
+        // opaque per tile: the 64 store addresses are formed here, not hoisted
+        // out of the stage loop into registers that would then spill
+        asm volatile("" : "+v"(vo));
+        asm volatile("" : "+s"(ld2));
+        const int64_t trel = tgt[ti] - vw - 4 * half;   // target as (vi, r) offset, if here
+#pragma unroll
+        for (int vi = 0; vi < 4; ++vi)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int k = vi * 32 + 8 * (r >> 2) + (r & 3);      // column - vw - 4 half
+            float dz = exp2_hw((acc[vi][ti][r] - g_lse_row[ti]) * kLog2e) * g_coef[ti];
+            if (trel == k) dz += g_tgt[ti];
+            // the whole offset goes in the vector operand: the range check
+            // (which drops the columns past V) does not see the scalar one
+            __builtin_amdgcn_raw_buffer_store_b16(bf16_rne(dz), rs_dz,
+                                                   vo + (uint32_t)k * ld2, 0, 0);
+          }
+      }
+      init_acc(v + 1);
+      continue;
+    }
     if (vbase + kVtileCols > p.V) {                // vocabulary tail: mask columns >= V
 #pragma unroll
       for (int vi = 0; vi < 4; ++vi)
@@ -426,6 +483,8 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
   // let them land before the workgroup's LDS is released.
   wait_vmcnt<0>();
 
+  if constexpr (kGrad) return;
+
   // ---- split done: merge lane halves, then the two vocabulary-half waves ----
   float mm[2], ss[2];
 #pragma unroll
@@ -455,10 +514,42 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
 }
 
 __global__ __launch_bounds__(kThreads, 1) void proj_lse_kernel(const ProjParams p) {
-  proj_lse_body<false>(p);
+  proj_lse_body<false, false>(p);
 }
 __global__ __launch_bounds__(kThreads, 1) void proj_lse_bias_kernel(const ProjParams p) {
-  proj_lse_body<true>(p);
+  proj_lse_body<true, false>(p);
+}
+__global__ __launch_bounds__(kThreads, 1) void softmax_grad_kernel(const ProjParams p) {
+  proj_lse_body<false, true>(p);
+}
+__global__ __launch_bounds__(kThreads, 1) void softmax_grad_bias_kernel(const ProjParams p) {
+  proj_lse_body<true, true>(p);
+}
+
+// Zero columns [N, ldz) of every row of dZ^T (the padding the GEMMs read).
+__global__ __launch_bounds__(256) void zero_pad_cols_kernel(uint16_t* __restrict__ dzt,
+                                                            int64_t rows, int64_t N, int64_t ldz) {
+  const int64_t pad = ldz - N;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * pad) return;
+  const int64_t r = i / pad;
+  dzt[r * ldz + N + (i - r * pad)] = 0;
+}
+
+// out[r] = sum over n = 0 .. N-1 of dZ^T[r][n]: one wave per row; lane k adds
+// n = k, k + 64, ... in ascending order, then a fixed pairwise tree.
+__global__ __launch_bounds__(256) void row_sums_kernel(const uint16_t* __restrict__ dzt,
+                                                       int64_t rows, int64_t N, int64_t ldz,
+                                                       float* __restrict__ out) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= rows) return;                    // uniform across the wave
+  const uint16_t* row = dzt + r * ldz;
+  float s = 0.f;
+  for (int64_t n = lane; n < N; n += 64) s += __uint_as_float((uint32_t)row[n] << 16);
+#pragma unroll
+  for (int d = 1; d <= 32; d <<= 1) s += __shfl_xor(s, d);
+  if (lane == 0) out[r] = s;
 }
 
 // Exact fp32 copy of the bias (bf16 widens exactly), zero-padded to whole
@@ -483,6 +574,34 @@ hipError_t launch_bias_f32(const void* bias, int32_t kind, int32_t V, float* out
   const int32_t padded = (V + kVtileCols - 1) / kVtileCols * kVtileCols;
   hipLaunchKernelGGL(bias_to_f32_kernel, dim3((unsigned)(padded / 256)), dim3(256), 0, stream,
                      bias, kind, V, padded, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_softmax_grad(const ProjParams& p, hipStream_t stream) {
+  const int64_t blocks = (int64_t)p.R * p.S;
+  if (blocks <= 0) return hipSuccess;
+  if (p.bias_kind != kBiasNone)
+    hipLaunchKernelGGL(softmax_grad_bias_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL(softmax_grad_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_pad_cols(uint16_t* dzt, int64_t rows, int64_t N, int64_t ldz,
+                                hipStream_t stream) {
+  const int64_t total = rows * (ldz - N);
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_pad_cols_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                     stream, dzt, rows, N, ldz);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_sums(const uint16_t* dzt, int64_t rows, int64_t N, int64_t ldz, float* out,
+                           hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(row_sums_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, dzt,
+                     rows, N, ldz, out);
   return hipGetLastError();
 }
 

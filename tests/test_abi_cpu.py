@@ -309,3 +309,93 @@ def test_det_gemm_wrappers_reject_bad_inputs():
         ila.det_gemm_da(torch.zeros(4, 3, dtype=torch.bfloat16), a)     # N mismatch
     with pytest.raises(ValueError):
         ila.det_gemm_db(a, torch.zeros(5, 8, dtype=torch.bfloat16))     # M mismatch
+
+
+# ------------------------------------------------------------- backward checks
+def test_backward_workspace_bytes():
+    def up(x):
+        return (x + 255) // 256 * 256
+    for N, V in [(1, 1000), (7, 1000), (8, 257), (4096, 128256), (1 << 21, 1000)]:
+        ldz = (N + 7) // 8 * 8
+        padded = (V + 255) // 256 * 256
+        assert ila.bilogp_backward_workspace_bytes(N, V) == up(2 * V * ldz) + up(4 * padded)
+    assert ila.bilogp_backward_workspace_bytes(0, 1000) == up(4 * 1024)
+    big = (1 << 64) - 1
+    assert ila.bilogp_backward_workspace_bytes(-1, 1000) == big
+    assert ila.bilogp_backward_workspace_bytes((1 << 21) + 1, 1000) == big
+    assert ila.bilogp_backward_workspace_bytes(8, 0) == big
+    assert ila.bilogp_backward_workspace_bytes(8, (1 << 30) + 1) == big
+
+
+def _call_bwd(hidden=FAKE, weight=FAKE + 0x100000, target=FAKE + 0x200000, bias=None,
+              bias_dtype=0, lse=FAKE + 0x300000, glogp=FAKE + 0x310000, glse=FAKE + 0x320000,
+              gh=FAKE + 0x400000, gw=FAKE + 0x1000000, gb=None, N=8, H=64, V=1000,
+              ws=FAKE + 0x2000000, ws_bytes=1 << 20):
+    lib = ila.load_library()
+    return lib.bilogp_backward(hidden, weight, target, bias, bias_dtype, lse, glogp, glse, gh,
+                               gw, gb, N, H, V, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=None), B.BILOGP_E_INVALID_ARG),
+    (dict(weight=None), B.BILOGP_E_INVALID_ARG),
+    (dict(target=None), B.BILOGP_E_INVALID_ARG),
+    (dict(lse=None), B.BILOGP_E_INVALID_ARG),
+    (dict(glogp=None), B.BILOGP_E_INVALID_ARG),
+    (dict(glse=None), B.BILOGP_E_INVALID_ARG),
+    (dict(gh=None), B.BILOGP_E_INVALID_ARG),
+    (dict(gw=None), B.BILOGP_E_INVALID_ARG),
+    (dict(N=-1), B.BILOGP_E_INVALID_ARG),
+    (dict(N=(1 << 21) + 1), B.BILOGP_E_INVALID_ARG),
+    (dict(H=0), B.BILOGP_E_INVALID_ARG),
+    (dict(V=0), B.BILOGP_E_INVALID_ARG),
+    (dict(V=(1 << 30) + 1), B.BILOGP_E_INVALID_ARG),
+    (dict(bias_dtype=7, bias=FAKE + 0x600000), B.BILOGP_E_UNSUPPORTED),
+    (dict(bias_dtype=2), B.BILOGP_E_INVALID_ARG),
+    (dict(bias=FAKE + 0x600000), B.BILOGP_E_INVALID_ARG),
+    (dict(H=60), B.BILOGP_E_UNSUPPORTED),
+    (dict(hidden=FAKE + 8), B.BILOGP_E_UNSUPPORTED),
+    (dict(gw=FAKE + 0x1000008), B.BILOGP_E_UNSUPPORTED),
+    (dict(target=FAKE + 0x200004), B.BILOGP_E_UNSUPPORTED),
+    (dict(lse=FAKE + 0x300002), B.BILOGP_E_UNSUPPORTED),
+    (dict(gb=FAKE + 0x700002), B.BILOGP_E_UNSUPPORTED),
+    (dict(ws=None), B.BILOGP_E_WORKSPACE),
+    (dict(ws_bytes=100), B.BILOGP_E_WORKSPACE),
+    (dict(ws=FAKE + 0x2000010), B.BILOGP_E_WORKSPACE),
+    (dict(gh=FAKE + 0x1000000), B.BILOGP_E_INVALID_ARG),          # gradients alias
+    (dict(gb=FAKE + 0x400000), B.BILOGP_E_INVALID_ARG),           # bias grad in grad_hidden
+    (dict(gh=FAKE), B.BILOGP_E_INVALID_ARG),                      # aliases hidden
+    (dict(gw=FAKE + 0x300000), B.BILOGP_E_INVALID_ARG),           # overlaps lse
+    (dict(gw=FAKE + 0x2000000), B.BILOGP_E_INVALID_ARG),          # overlaps the workspace
+])
+def test_backward_fails_closed(kw, status):
+    st = _call_bwd(**kw)
+    assert st == status, (kw, st, ila.bilogp_last_error())
+    assert ila.bilogp_last_error() != ""
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU path")
+def test_backward_no_device_is_unsupported():
+    assert _call_bwd() == B.BILOGP_E_UNSUPPORTED
+    # an empty batch still writes the (zero) weight gradient: it needs the device
+    assert _call_bwd(N=0, hidden=None, target=None, lse=None, glogp=None, glse=None,
+                     gh=None) == B.BILOGP_E_UNSUPPORTED
+
+
+def test_backward_wrapper_rejects_bad_inputs():
+    h = torch.zeros(4, 16, dtype=torch.bfloat16)
+    w = torch.zeros(32, 16, dtype=torch.bfloat16)
+    t = torch.zeros(4, dtype=torch.int64)
+    f = torch.zeros(4)
+    with pytest.raises(TypeError):
+        ila.backward(h.float(), w, t, None, f, f, f)
+    with pytest.raises(TypeError):
+        ila.backward(h, w, t, None, f.double(), f, f)
+    with pytest.raises(ValueError):
+        ila.backward(h, w, t[:3], None, f, f, f)
+    with pytest.raises(ValueError):
+        ila.backward(h, w, t, torch.zeros(31), f, f, f)
+    with pytest.raises(ValueError):
+        ila.backward(h, w, t, None, f, f, f)                  # not on a GPU
+    with pytest.raises(ValueError):
+        ila.backward_workspace_for((1 << 21) + 1, 32, "cpu")
