@@ -401,29 +401,40 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
       const int vrows = min(kVtileCols, p.V - vbase);
       const __amdgpu_buffer_rsrc_t rs_dz = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(p.dzt + (int64_t)vbase * p.ldz), (short)0, vrows * (int)p.ldz * 2, kRsrcWord3);
+      // per token column: its row, whether it exists, the store offset and
+      // the target's (vi, r) offset relative to this lane's first column
+      uint32_t vo[2];
+      bool live[2];
+      int64_t trel[2];
 #pragma unroll
       for (int ti = 0; ti < 2; ++ti) {
         const int jr = wt * 64 + ti * 32 + (lane & 31);
-        if (jr >= rows_here) continue;
-        uint32_t vo = ((uint32_t)(wv * 128 + 4 * half) * (uint32_t)p.ldz + (uint32_t)(m0 + jr)) * 2u;
-        uint32_t ld2 = (uint32_t)p.ldz * 2u;
-        // opaque per tile: the 64 store addresses are formed here, not hoisted
+        live[ti] = jr < rows_here;
+        vo[ti] = ((uint32_t)(wv * 128 + 4 * half) * (uint32_t)p.ldz + (uint32_t)(m0 + jr)) * 2u;
+        // opaque per tile: the store addresses are formed here, not hoisted
         // out of the stage loop into registers that would then spill
-        asm volatile("" : "+v"(vo));
-        asm volatile("" : "+s"(ld2));
-        const int64_t trel = tgt[ti] - vw - 4 * half;   // target as (vi, r) offset, if here
+        asm volatile("" : "+v"(vo[ti]));
+        trel[ti] = tgt[ti] - vw - 4 * half;
+      }
+      uint32_t ld2 = (uint32_t)p.ldz * 2u;
+      asm volatile("" : "+s"(ld2));
+      // both token columns of a vocabulary row back to back: the two 64-byte
+      // halves of each 128-byte line of dZ^T leave together
 #pragma unroll
-        for (int vi = 0; vi < 4; ++vi)
+      for (int vi = 0; vi < 4; ++vi) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int k = vi * 32 + 8 * (r >> 2) + (r & 3);      // column - vw - 4 half
+        for (int r = 0; r < 16; ++r) {
+          const int k = vi * 32 + 8 * (r >> 2) + (r & 3);      // column - vw - 4 half
+#pragma unroll
+          for (int ti = 0; ti < 2; ++ti) {
             float dz = exp2_hw((acc[vi][ti][r] - g_lse_row[ti]) * kLog2e) * g_coef[ti];
-            if (trel == k) dz += g_tgt[ti];
-            // the whole offset goes in the vector operand: the range check
-            // (which drops the columns past V) does not see the scalar one
-            __builtin_amdgcn_raw_buffer_store_b16(bf16_rne(dz), rs_dz,
-                                                   vo + (uint32_t)k * ld2, 0, 0);
+            if (trel[ti] == k) dz += g_tgt[ti];
+            if (live[ti])
+              __builtin_amdgcn_raw_buffer_store_b16(bf16_rne(dz), rs_dz, vo[ti] + (uint32_t)k * ld2,
+                                                     0, 0);
           }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
       init_acc(v + 1);
       continue;

@@ -63,6 +63,19 @@ def test_ragged_full(N, H, V, bias, seed):
         assert torch.all(logp == 0)
 
 
+@pytest.mark.parametrize("N,H,V,bias,seed", [
+    (300, 65536, 2000, "f32", 108),    # wide K: 1024 stages per tile, byte offsets near 2^27
+    (100003, 64, 1000, None, 109),     # 391 row blocks, ragged last block
+])
+def test_large_dims_full(N, H, V, bias, seed):
+    inp = synth.make_custom(N, H, V, seed=seed, bias=bias, device=DEV)
+    say(f"large dims N={N} H={H} V={V} bias={bias}")
+    logp, lse = run_inputs(inp)
+    torch.cuda.synchronize()
+    ref_lp, ref_ls = oracle_rows(inp)
+    assert_parity(logp, lse, ref_lp, ref_ls, what=f"large N={N} H={H} V={V}")
+
+
 @pytest.mark.parametrize("name,k", [("headline", 512), ("sweep", 256)])
 def test_large_sampled(name, k):
     inp = synth.make_inputs(name, device=DEV)
