@@ -4,7 +4,7 @@ one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline]
                     [--no-cpu-baseline] [--no-backward] [--no-det-gemm]
-                    [--no-invariance-cost]
+                    [--no-invariance-cost] [--no-shard-share]
 
 One step is one full pass of the hot path over one batch: bilogp_partials
 (fused bf16-MFMA projection + per-split online softmax) followed by
@@ -39,7 +39,7 @@ PEAK_HBM_GBPS = 8000.0
 # reads for a plain 1 GiB device copy (x2.000 and x1.000).  Keyed by the sha256 prefix
 # of the kernel source the counters were taken on: any other source reports null.
 MEASURED_TRAFFIC = {
-    ("headline", "b85c197782f69b59"): {"fetch_bytes": 6619181153, "write_bytes": 3133992},
+    ("headline", "2473453cd2073459"): {"fetch_bytes": 6622846077, "write_bytes": 3114592},
 }
 
 
@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-det-gemm", action="store_true",
                     help="skip timing the deterministic GEMM (forward, dA, dB)")
+    ap.add_argument("--no-shard-share", action="store_true",
+                    help="skip timing one GPU's share of an 8-way vocabulary or row sharding")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip timing the deterministic backward")
     ap.add_argument("--no-invariance-cost", action="store_true",
@@ -199,6 +201,81 @@ def backward_leg(h, t, w, b, lse, steps=10, warmup=3):
             "finite": bool(torch.isfinite(gh).all()) and bool(torch.isfinite(gw).all())}
 
 
+def shard_share_leg(h, t, w, b, ranks=8, steps=10, warmup=3):
+    """One GPU's share of the workload sharded over `ranks` GPUs, at its real
+    shape: (a) vocabulary sharding - rank 0's contiguous split range of the
+    full V (bilogp_partials_range on its own weight columns), (b) row sharding
+    - the full step on N / ranks rows.  No exchange is timed (one GPU)."""
+    import torch
+    import invariant_linear_log_amd as ila
+    dev = h.device
+    N, H = h.shape
+    V = w.shape[0]
+    S = ila.bilogp_num_vocab_splits(V)
+    per = -(-S // ranks)
+    c0, c1 = ila.vocab_split_columns(V, 0, per)
+    w_slice = w[c0:c1].clone()
+    b_slice = None if b is None else b[c0:c1].clone()
+    ws = ila.workspace_for(N, V, dev)
+    stream = torch.cuda.Stream(device=dev)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    vs_ms = timed(lambda: ila.bilogp_partials_range(h, w_slice, t, b_slice, V, 0, per, ws,
+                                                    stream=stream))
+    n = -(-N // ranks)
+    hn, tn = h[:n].contiguous(), t[:n].contiguous()
+    lp = torch.empty(n, device=dev)
+    ls = torch.empty(n, device=dev)
+    wsn = ila.workspace_for(n, V, dev)
+    ns_ms = timed(lambda: ila.bilogp_forward_ex(hn, w, tn, b, lp, ls, wsn, stream=stream))
+    fv = 2.0 * N * H * (c1 - c0)
+    fn_ = 2.0 * n * H * V
+    return {"ranks": ranks,
+            "vocab_shard": {"splits": [0, per], "columns": [c0, c1], "ms": vs_ms,
+                            "tflops": fv / vs_ms / 1e9, "frac": fv / vs_ms / 1e9 / PEAK_BF16_TFLOPS},
+            "row_shard": {"rows": n, "ms": ns_ms, "tflops": fn_ / ns_ms / 1e9,
+                          "frac": fn_ / ns_ms / 1e9 / PEAK_BF16_TFLOPS}}
+
+
+def device_info(dev):
+    import torch
+    prop = torch.cuda.get_device_properties(dev)
+    return {"name": prop.name, "arch": getattr(prop, "gcnArchName", ""),
+            "compute_units": prop.multi_processor_count,
+            "hbm_gib": round(prop.total_memory / 2 ** 30, 1)}
+
+
+def cpu_info():
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    blas = ""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = ",".join(sorted({i.get("internal_api", "") for i in threadpool_info()
+                                if i.get("user_api") == "blas"}))
+    except Exception:  # pragma: no cover
+        pass
+    return model, blas
+
+
 def cpu_baseline(inp, rows_n, seed=7):
     import numpy as np
     import oracle
@@ -218,9 +295,12 @@ def cpu_baseline(inp, rows_n, seed=7):
     t0 = time.perf_counter()
     oracle.linear_logp(h, w, t, b, rows=rows)
     dt = time.perf_counter() - t0
+    model, blas = cpu_info()
+    flops = 2.0 * len(rows) * h.shape[1] * w.shape[0]
     return {"value": len(rows) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{len(rows)} seeded rows of the {N}-row workload (fp64 numpy/BLAS, "
-                      f"bf16 decode included), {dt:.1f} s"}
+                      f"bf16 decode included), {dt:.1f} s",
+            "fp64_gflops": flops / dt / 1e9, "cpu": model, "blas": blas}
 
 
 def main():
@@ -277,6 +357,7 @@ def main():
 
     proj_ms = [e[0].elapsed_time(e[1]) for e in evs]
     merge_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    step_ms = sorted(e[0].elapsed_time(e[2]) for e in evs)
     avg_proj_s = sum(proj_ms) / K / 1e3
     avg_merge_s = sum(merge_ms) / K / 1e3
     flops = 2.0 * N * H * V
@@ -305,13 +386,18 @@ def main():
                    "bias": wl.bias, "splits": S, "tokens_per_step": N},
         "tflops": tflops_step,
         "mfma_peak_frac": tflops_step / PEAK_BF16_TFLOPS,
-        "kernel_ms": {"proj_lse": avg_proj_s * 1e3, "merge": avg_merge_s * 1e3},
+        "kernel_ms": {"proj_lse": avg_proj_s * 1e3, "merge": avg_merge_s * 1e3,
+                      "proj_lse_median": sorted(proj_ms)[K // 2], "proj_lse_min": min(proj_ms),
+                      "step_median": step_ms[K // 2], "step_min": step_ms[0]},
+        "device": device_info(dev),
         "outputs_sane": ok,
         "roofline": {"bound": "mfma", "kernel": "proj_lse_kernel",
                      "achieved": tflops_proj, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops_proj / PEAK_BF16_TFLOPS,
                      "algorithmic_flops": flops,
                      "algorithmic_bytes": algorithmic_bytes(N, H, V, S, bias_bytes),
+                     "algorithmic_hbm_gbps": algorithmic_bytes(N, H, V, S, bias_bytes)
+                     / avg_proj_s / 1e9,
                      "traffic": measured_traffic(wl.name),
                      "traffic_unit": "bytes per launch"},
     }
@@ -319,6 +405,8 @@ def main():
         out["invariance_cost"] = invariance_cost(h, t, w, b)
     if not args.no_backward:
         out["backward"] = backward_leg(h, t, w, b, lse)
+    if not args.no_shard_share:
+        out["shard_share"] = shard_share_leg(h, t, w, b)
     if not args.no_det_gemm:
         out["det_gemm"] = det_gemm_leg()
     if not args.no_cpu_baseline:

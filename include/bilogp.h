@@ -184,6 +184,37 @@ bilogp_status bilogp_partials(const void* hidden, const void* weight, const int6
                               const void* bias, int bias_dtype, int64_t N, int64_t H, int64_t V,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* bilogp_partials_range: one rank's share of a vocabulary-sharded projection.
+ * The split boundaries depend on the full V alone (PR #337, description,
+ * "What this PR changes", and the annotation on
+ * select_batch_invariant_vocab_splits), so every rank of a vocabulary-sharded
+ * lm-head agrees on them without communicating.  A rank holding the
+ * vocabulary columns of splits [split_begin, split_end) runs the projection
+ * and per-split online softmax of those splits only:
+ *
+ *   weight_slice  bf16 [c1 - c0, H], columns [c0, c1) of the full weight, with
+ *                 c0 = split_begin * vps * tile width and
+ *                 c1 = min(split_end * vps * tile width, V), vps =
+ *                 bilogp_vtiles_per_split(V); 16-byte aligned
+ *   bias_slice    the same columns of the bias (bf16 or fp32), or NULL
+ *   V             the FULL vocabulary size; 0 <= split_begin < split_end <=
+ *                 bilogp_num_vocab_splits(V), else BILOGP_E_INVALID_ARG
+ *   workspace     the layout of bilogp_workspace_bytes(N, V) (partials first,
+ *                 row-major [N][S] (max, sum) float pairs; then the [N] target
+ *                 logits); the call writes its splits' columns of the
+ *                 partials and the target logit of each row whose target lies
+ *                 in [c0, c1), and nothing else
+ *
+ * Once every split's columns are present - written by calls on this device,
+ * or copied in from the other ranks - bilogp_merge gives bit for bit the
+ * result of bilogp_forward_ex on the full weight.  Other arguments and checks
+ * as for bilogp_partials.  The exchange between ranks is the caller's. */
+bilogp_status bilogp_partials_range(const void* hidden, const void* weight_slice,
+                                    const int64_t* target, const void* bias_slice, int bias_dtype,
+                                    int64_t N, int64_t H, int64_t V, int split_begin,
+                                    int split_end, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
 /* bilogp_merge: the ascending combine of the partials left in `workspace` by
  * bilogp_partials for the same N, V and target (PR #337, description:
  * "ascending combine"); writes logp_out and lse_out, fp32 [N]. */

@@ -60,6 +60,7 @@ from ._binding import (  # noqa: F401
     bilogp_num_vocab_splits,
     bilogp_num_vocab_splits_mode,
     bilogp_partials,
+    bilogp_partials_range,
     bilogp_status_string,
     bilogp_vtile_cols,
     bilogp_vtiles_per_split,
@@ -67,6 +68,7 @@ from ._binding import (  # noqa: F401
     bilogp_workspace_bytes,
     bilogp_workspace_bytes_mode,
     load_library,
+    vocab_split_columns,
 )
 
 from .det_gemm import DetLinear, det_gemm, det_gemm_da, det_gemm_db  # noqa: F401,E402

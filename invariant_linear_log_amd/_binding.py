@@ -60,6 +60,9 @@ SIGNATURES = {
     "bilogp_partials": (ctypes.c_int, [_VP, _VP, _VP, _VP, ctypes.c_int, _I64, _I64, _I64, _VP,
                                        ctypes.c_size_t, _VP]),
     "bilogp_merge": (ctypes.c_int, [_VP, _VP, ctypes.c_size_t, _VP, _VP, _I64, _I64, _VP]),
+    "bilogp_partials_range": (ctypes.c_int, [_VP, _VP, _VP, _VP, ctypes.c_int, _I64, _I64, _I64,
+                                             ctypes.c_int, ctypes.c_int, _VP, ctypes.c_size_t,
+                                             _VP]),
     "bilogp_det_gemm_fwd": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64, ctypes.c_int, _VP]),
     "bilogp_det_gemm_da": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64, ctypes.c_int, _VP]),
     "bilogp_det_gemm_db": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64, ctypes.c_int, _VP]),
@@ -240,6 +243,32 @@ def bilogp_partials(hidden: torch.Tensor, weight: torch.Tensor, target: torch.Te
                                  workspace.numel() * workspace.element_size(),
                                  _stream_handle(stream, hidden.device))
     _check(st)
+
+
+def bilogp_partials_range(hidden: torch.Tensor, weight_slice: torch.Tensor,
+                          target: torch.Tensor, bias_slice: Optional[torch.Tensor], V: int,
+                          split_begin: int, split_end: int, workspace: torch.Tensor,
+                          stream=None) -> None:
+    """``bilogp_partials_range``: partials of splits [split_begin, split_end)
+    of the full vocabulary V from that range's weight (and bias) columns."""
+    N, H = hidden.shape
+    lib = load_library()
+    with torch.cuda.device(hidden.device):
+        st = lib.bilogp_partials_range(_ptr(hidden), _ptr(weight_slice), _ptr(target),
+                                       _ptr(bias_slice), _bias_dtype(bias_slice), N, H, V,
+                                       split_begin, split_end, _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream_handle(stream, hidden.device))
+    _check(st)
+
+
+def vocab_split_columns(V: int, split_begin: int, split_end: int):
+    """Vocabulary columns [c0, c1) of splits [split_begin, split_end) under
+    the V-only policy (the columns bilogp_partials_range's weight slice holds)."""
+    lib = load_library()
+    vps = lib.bilogp_vtiles_per_split(V)
+    tile = lib.bilogp_vtile_cols()
+    return split_begin * vps * tile, min(split_end * vps * tile, V)
 
 
 def bilogp_merge(target: torch.Tensor, workspace: torch.Tensor, logp_out: torch.Tensor,

@@ -200,6 +200,10 @@ struct Call {
   size_t ws_bytes;
   int mode = BILOGP_SPLITS_INVARIANT;
   int cu_count = 0;
+  // projection over splits [split_begin, split_end) only (split_end < 0: all);
+  // weight and bias then hold just those splits' vocabulary columns
+  int split_begin = 0;
+  int split_end = -1;
 };
 
 // Full argument validation (fail closed) and the launch parameters.  Pure
@@ -234,19 +238,32 @@ bilogp_status validate(const Call& c, int parts, bilogp::ProjParams* out) {
     return fail(BILOGP_E_UNSUPPORTED, "target must be 8-byte aligned");
   if (merge && (reinterpret_cast<uintptr_t>(c.logp) | reinterpret_cast<uintptr_t>(c.lse)) % 4)
     return fail(BILOGP_E_UNSUPPORTED, "outputs must be 4-byte aligned");
+  if (c.split_end >= 0) {      // split ranges exist for the V-only policy alone
+    const int S_inv = bilogp_num_vocab_splits(c.V);
+    if (c.mode != BILOGP_SPLITS_INVARIANT || c.split_begin < 0 ||
+        c.split_begin >= c.split_end || c.split_end > S_inv)
+      return fail(BILOGP_E_INVALID_ARG, "split range must satisfy 0 <= begin < end <= " +
+                                            std::to_string(S_inv));
+  }
   if (c.N == 0) return BILOGP_OK;
 
   const int S = bilogp_num_vocab_splits_mode(c.N, c.V, c.mode, c.cu_count);
+  const int vps = bilogp_vtiles_per_split_mode(c.N, c.V, c.mode, c.cu_count);
   const int64_t R = (c.N + bilogp::kBlockRows - 1) / bilogp::kBlockRows;
   if (R * S > INT32_MAX) return fail(BILOGP_E_INVALID_ARG, "N too large for one launch");
+  // vocabulary columns [col0, col1) that weight and bias hold
+  const bool ranged = c.split_end >= 0;
+  const int64_t col0 = ranged ? (int64_t)c.split_begin * vps * bilogp::kVtileCols : 0;
+  const int64_t col1 =
+      ranged ? std::min<int64_t>((int64_t)c.split_end * vps * bilogp::kVtileCols, c.V) : c.V;
 
   if (merge) {
     const Range r_logp = range_of(c.logp, (size_t)c.N * 4), r_lse = range_of(c.lse, (size_t)c.N * 4);
     const Range others[] = {
         proj ? range_of(c.hidden, (size_t)c.N * c.H * 2) : Range{0, 0},
-        proj ? range_of(c.weight, (size_t)c.V * c.H * 2) : Range{0, 0},
+        proj ? range_of(c.weight, (size_t)(col1 - col0) * c.H * 2) : Range{0, 0},
         range_of(c.target, (size_t)c.N * 8),
-        (proj && c.bias) ? range_of(c.bias, (size_t)c.V * bias_esz) : Range{0, 0},
+        (proj && c.bias) ? range_of(c.bias, (size_t)(col1 - col0) * bias_esz) : Range{0, 0},
         c.ws ? range_of(c.ws, c.ws_bytes) : Range{0, 0}};
     if (overlap(r_logp, r_lse)) return fail(BILOGP_E_INVALID_ARG, "logp_out and lse_out overlap");
     for (const Range& in : others)
@@ -276,9 +293,14 @@ bilogp_status validate(const Call& c, int parts, bilogp::ProjParams* out) {
   const WsLayout L = ws_layout(c.ws, c.N, S);
   bilogp::ProjParams& p = *out;
   p.hidden = c.hidden;
-  p.weight = c.weight;
+  // absolute-column addressing: shift the slice's base back by col0 columns
+  // (unsigned arithmetic; the kernel adds them again before any access)
+  p.weight = reinterpret_cast<const void*>(reinterpret_cast<uintptr_t>(c.weight) -
+                                           (uintptr_t)col0 * (uintptr_t)c.H * 2u);
   p.target = c.target;
-  p.bias = c.bias ? L.bias32 : nullptr;   // the kernel reads the padded fp32 copy
+  p.bias = c.bias ? reinterpret_cast<const float*>(reinterpret_cast<uintptr_t>(L.bias32) -
+                                                    (uintptr_t)col0 * sizeof(float))
+                  : nullptr;   // the kernel reads the padded fp32 copy
   p.part = L.part;
   p.tlogit = L.tlogit;
   p.N = c.N;
@@ -288,9 +310,12 @@ bilogp_status validate(const Call& c, int parts, bilogp::ProjParams* out) {
                 : c.bias_dtype == BILOGP_BIAS_F32 ? bilogp::kBiasF32
                                                   : bilogp::kBiasNone;
   p.T = (int32_t)((c.V + bilogp::kVtileCols - 1) / bilogp::kVtileCols);
-  p.vps = bilogp_vtiles_per_split_mode(c.N, c.V, c.mode, c.cu_count);
+  p.vps = vps;
   p.S = S;
   p.R = (int32_t)R;
+  p.split0 = ranged ? c.split_begin : 0;
+  p.S_grid = ranged ? c.split_end - c.split_begin : S;
+  p.col0 = col0;
   return BILOGP_OK;
 }
 
@@ -299,8 +324,14 @@ bilogp_status launch(const bilogp::ProjParams& p, const Call& c, int parts, void
   float* logp = c.logp;
   float* lse = c.lse;
   if ((parts & kProj) && c.bias) {
-    hipError_t e = bilogp::launch_bias_f32(c.bias, p.bias_kind, p.V,
-                                           const_cast<float*>(static_cast<const float*>(p.bias)), s);
+    // the padded fp32 copy of the bias columns the launch reads, from col0
+    const int64_t cols = c.split_end >= 0
+        ? std::min<int64_t>((int64_t)(p.split0 + p.S_grid) * p.vps * bilogp::kVtileCols, p.V) -
+              p.col0
+        : p.V;
+    float* bias32 = reinterpret_cast<float*>(reinterpret_cast<uintptr_t>(p.bias) +
+                                             (uintptr_t)p.col0 * sizeof(float));
+    hipError_t e = bilogp::launch_bias_f32(c.bias, p.bias_kind, (int32_t)cols, bias32, s);
     if (e != hipSuccess)
       return fail(BILOGP_E_HIP, std::string("bias copy launch: ") + hipGetErrorString(e));
   }
@@ -355,6 +386,18 @@ bilogp_status bilogp_partials(const void* hidden, const void* weight, const int6
                               void* workspace, size_t workspace_bytes, void* stream) {
   const Call c{hidden, weight, target, bias, bias_dtype, nullptr, nullptr,
                N,      H,      V,      workspace, workspace_bytes};
+  return run(c, kProj, stream);
+}
+
+bilogp_status bilogp_partials_range(const void* hidden, const void* weight_slice,
+                                    const int64_t* target, const void* bias_slice, int bias_dtype,
+                                    int64_t N, int64_t H, int64_t V, int split_begin,
+                                    int split_end, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  Call c{hidden, weight_slice, target, bias_slice, bias_dtype, nullptr, nullptr,
+         N,      H,            V,      workspace,  workspace_bytes};
+  c.split_begin = split_begin;
+  c.split_end = split_end < 0 ? 0 : split_end;   // a negative end is an empty (invalid) range
   return run(c, kProj, stream);
 }
 
@@ -603,6 +646,9 @@ bilogp_status bilogp_backward(const void* hidden, const void* weight, const int6
       p.vps = bilogp_vtiles_per_split(V);
       p.S = bilogp_num_vocab_splits(V);
       p.R = (int32_t)((N + bilogp::kBlockRows - 1) / bilogp::kBlockRows);
+      p.split0 = 0;
+      p.S_grid = p.S;
+      p.col0 = 0;
       p.lse = lse;
       p.g_logp = grad_logp;
       p.g_lse = grad_lse;

@@ -35,6 +35,14 @@ struct ProjParams {
   int32_t vps;             // tiles per split
   int32_t S;               // splits
   int32_t R;               // row blocks, ceil(N / kBlockRows)
+  // the launch covers splits [split0, split0 + S_grid) of the S.  weight and
+  // bias are addressed by absolute vocabulary column: for a launch whose
+  // weight holds columns from col0 on, the host passes the weight address
+  // minus col0 rows (and the bias copy's address minus col0 entries); every
+  // address the kernel forms stays inside the slice
+  int32_t split0;
+  int32_t S_grid;
+  int64_t col0;
   // backward only (softmax-gradient kernel): the forward's lse, the upstream
   // gradients of logp and lse, and dZ^T [V, ldz] (bf16) written per tile
   const float* lse;

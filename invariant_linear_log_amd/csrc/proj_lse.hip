@@ -157,15 +157,15 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
   // run of tile indices, then order tiles in groups of kRowBlockGroup row
   // blocks x all splits (row blocks fastest), so the ~32 tiles an XCD runs at
   // once share a few W slices and a few hidden blocks in its L2.
-  const int nblk = p.R * p.S;
+  const int nblk = p.R * p.S_grid;
   const int per_xcd = nblk >> 3;
   int u = blockIdx.x;
   if (u < (per_xcd << 3)) u = (u & 7) * per_xcd + (u >> 3);
-  const int in_group = kRowBlockGroup * p.S;
+  const int in_group = kRowBlockGroup * p.S_grid;
   const int first_rb = (u / in_group) * kRowBlockGroup;
   const int group_rbs = min(p.R - first_rb, kRowBlockGroup);
   const int rb = first_rb + (u % in_group) % group_rbs;
-  const int split = (u % in_group) / group_rbs;
+  const int split = p.split0 + (u % in_group) / group_rbs;
 
   const int64_t m0 = (int64_t)rb * kBlockRows;
   const int rows_here = (int)min((int64_t)kBlockRows, p.N - m0);
@@ -589,7 +589,7 @@ hipError_t launch_bias_f32(const void* bias, int32_t kind, int32_t V, float* out
 }
 
 hipError_t launch_softmax_grad(const ProjParams& p, hipStream_t stream) {
-  const int64_t blocks = (int64_t)p.R * p.S;
+  const int64_t blocks = (int64_t)p.R * p.S_grid;
   if (blocks <= 0) return hipSuccess;
   if (p.bias_kind != kBiasNone)
     hipLaunchKernelGGL(softmax_grad_bias_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
@@ -617,7 +617,7 @@ hipError_t launch_row_sums(const uint16_t* dzt, int64_t rows, int64_t N, int64_t
 }
 
 hipError_t launch_proj_lse(const ProjParams& p, hipStream_t stream) {
-  const int64_t blocks = (int64_t)p.R * p.S;
+  const int64_t blocks = (int64_t)p.R * p.S_grid;
   if (blocks <= 0) return hipSuccess;
   if (p.bias_kind != kBiasNone)
     hipLaunchKernelGGL(proj_lse_bias_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);

@@ -399,3 +399,30 @@ def test_backward_wrapper_rejects_bad_inputs():
         ila.backward(h, w, t, None, f, f, f)                  # not on a GPU
     with pytest.raises(ValueError):
         ila.backward_workspace_for((1 << 21) + 1, 32, "cpu")
+
+
+# ------------------------------------------------------------- split-range checks
+def _call_range(begin, end, N=8, V=128256, H=64, bias=None, bias_dtype=0):
+    lib = ila.load_library()
+    return lib.bilogp_partials_range(FAKE, FAKE + 0x100000, FAKE + 0x200000, bias, bias_dtype, N,
+                                     H, V, begin, end, FAKE + 0x40000000, 1 << 24, None)
+
+
+@pytest.mark.parametrize("begin,end", [(-1, 3), (3, 3), (5, 2), (0, 64), (62, 64), (0, -1)])
+def test_partials_range_rejects_bad_ranges(begin, end):
+    # V = 128256 has 63 splits
+    assert _call_range(begin, end) == B.BILOGP_E_INVALID_ARG, ila.bilogp_last_error()
+    assert _call_range(begin, end, N=0) == B.BILOGP_E_INVALID_ARG
+
+
+def test_partials_range_empty_batch_and_columns():
+    assert _call_range(0, 63, N=0) == B.BILOGP_OK
+    assert _call_range(10, 20, N=0) == B.BILOGP_OK
+    assert ila.vocab_split_columns(128256, 0, 63) == (0, 128256)
+    assert ila.vocab_split_columns(128256, 7, 9) == (7 * 8 * 256, 9 * 8 * 256)
+    assert ila.vocab_split_columns(1000, 3, 4) == (768, 1000)
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU path")
+def test_partials_range_no_device_is_unsupported():
+    assert _call_range(0, 8) == B.BILOGP_E_UNSUPPORTED
