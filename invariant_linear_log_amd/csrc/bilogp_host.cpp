@@ -58,9 +58,11 @@ WsLayout ws_layout(void* ws, int64_t N, int S) {
                   reinterpret_cast<float*>(b + o2)};
 }
 
-// Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other.
+// Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other;
+// and the device's compute-unit count (0 unknown).
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_ok[kMaxDevices];
+std::atomic<int> g_cu_count[kMaxDevices];
 
 bilogp_status check_device(int* dev_out) {
   int dev = -1;
@@ -75,6 +77,7 @@ bilogp_status check_device(int* dev_out) {
     if (e != hipSuccess)
       return fail(BILOGP_E_HIP, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
     st = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_cu_count[dev].store(prop.multiProcessorCount, std::memory_order_release);
     g_arch_ok[dev].store(st, std::memory_order_release);
     if (st != 1)
       return fail(BILOGP_E_UNSUPPORTED,
@@ -83,6 +86,16 @@ bilogp_status check_device(int* dev_out) {
   if (st != 1) return fail(BILOGP_E_UNSUPPORTED, "device architecture is not gfx950");
   *dev_out = dev;
   return BILOGP_OK;
+}
+
+// Row-block height of a projection launch: 256 tokens, or 128 when 256-token
+// blocks give fewer workgroups than the device has compute units.  A row's
+// arithmetic is the same in either (row blocking never changes bits), so the
+// choice may follow N and the device.
+int32_t row_block_rows(int64_t N, int64_t splits, int dev) {
+  const int cu = g_cu_count[dev].load(std::memory_order_acquire);
+  const int64_t r256 = (N + 255) / 256;
+  return (cu > 0 && r256 * splits < cu) ? 128 : 256;
 }
 
 bilogp_status check_on_device(const void* ptr, int dev, const char* name) {
@@ -249,7 +262,8 @@ bilogp_status validate(const Call& c, int parts, bilogp::ProjParams* out) {
 
   const int S = bilogp_num_vocab_splits_mode(c.N, c.V, c.mode, c.cu_count);
   const int vps = bilogp_vtiles_per_split_mode(c.N, c.V, c.mode, c.cu_count);
-  const int64_t R = (c.N + bilogp::kBlockRows - 1) / bilogp::kBlockRows;
+  // 256-token row blocks (128-token blocks are used only for small grids)
+  const int64_t R = (c.N + 255) / 256;
   if (R * S > INT32_MAX) return fail(BILOGP_E_INVALID_ARG, "N too large for one launch");
   // vocabulary columns [col0, col1) that weight and bias hold
   const bool ranged = c.split_end >= 0;
@@ -292,6 +306,7 @@ bilogp_status validate(const Call& c, int parts, bilogp::ProjParams* out) {
 
   const WsLayout L = ws_layout(c.ws, c.N, S);
   bilogp::ProjParams& p = *out;
+  p.rows = row_block_rows(c.N, ranged ? c.split_end - c.split_begin : S, dev);
   p.hidden = c.hidden;
   // absolute-column addressing: shift the slice's base back by col0 columns
   // (unsigned arithmetic; the kernel adds them again before any access)
@@ -312,7 +327,7 @@ bilogp_status validate(const Call& c, int parts, bilogp::ProjParams* out) {
   p.T = (int32_t)((c.V + bilogp::kVtileCols - 1) / bilogp::kVtileCols);
   p.vps = vps;
   p.S = S;
-  p.R = (int32_t)R;
+  p.R = (int32_t)((c.N + p.rows - 1) / p.rows);
   p.split0 = ranged ? c.split_begin : 0;
   p.S_grid = ranged ? c.split_end - c.split_begin : S;
   p.col0 = col0;
@@ -645,7 +660,8 @@ bilogp_status bilogp_backward(const void* hidden, const void* weight, const int6
       p.T = (int32_t)((V + bilogp::kVtileCols - 1) / bilogp::kVtileCols);
       p.vps = bilogp_vtiles_per_split(V);
       p.S = bilogp_num_vocab_splits(V);
-      p.R = (int32_t)((N + bilogp::kBlockRows - 1) / bilogp::kBlockRows);
+      p.rows = row_block_rows(N, p.S, dev);
+      p.R = (int32_t)((N + p.rows - 1) / p.rows);
       p.split0 = 0;
       p.S_grid = p.S;
       p.col0 = 0;

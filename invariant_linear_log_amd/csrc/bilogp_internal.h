@@ -34,7 +34,8 @@ struct ProjParams {
   int32_t T;               // vocabulary tiles, ceil(V / kVtileCols)
   int32_t vps;             // tiles per split
   int32_t S;               // splits
-  int32_t R;               // row blocks, ceil(N / kBlockRows)
+  int32_t rows;            // tokens per row block: 256, or 128 for small batches
+  int32_t R;               // row blocks, ceil(N / rows)
   // the launch covers splits [split0, split0 + S_grid) of the S.  weight and
   // bias are addressed by absolute vocabulary column: for a launch whose
   // weight holds columns from col0 on, the host passes the weight address

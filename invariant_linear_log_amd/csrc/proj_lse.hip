@@ -130,8 +130,12 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 // The kernel body, instantiated with and without bias, and (kGrad) as the
 // softmax-gradient pass of the backward: the same tiles and the same
 // accumulation, with an epilogue that writes dZ instead of reducing it.
-template <bool kHasBias, bool kGrad>
+template <bool kHasBias, bool kGrad, int kTi>
 __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
+  static_assert(kTi == 1 || kTi == 2, "one or two 32-token columns per wave");
+  constexpr int kRows = 128 * kTi;                 // tokens per row block
+  constexpr int kWaveTok = 32 * kTi;               // tokens per wave
+  constexpr int kLoadsH = kRows * kLdsRowBytes / (kThreads * 16);   // hidden loads per stage
   // Two LDS buffers, each its own variable, so the compiler can tell a read
   // of one from a direct-to-LDS load into the other and does not drain the
   // load pipeline before every read.  Buffer layout: W slice (32 KB), hidden
@@ -167,8 +171,8 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
   const int rb = first_rb + (u % in_group) % group_rbs;
   const int split = p.split0 + (u % in_group) / group_rbs;
 
-  const int64_t m0 = (int64_t)rb * kBlockRows;
-  const int rows_here = (int)min((int64_t)kBlockRows, p.N - m0);
+  const int64_t m0 = (int64_t)rb * kRows;
+  const int rows_here = (int)min((int64_t)kRows, p.N - m0);
   const int vt_begin = split * p.vps;
   const int nvt = min(vt_begin + p.vps, p.T) - vt_begin;
   const int H = p.H;
@@ -191,6 +195,16 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
     voff_base[j] = (uint32_t)r * (uint32_t)H * 2u + (uint32_t)cc * 16u;
     kchunk[j] = cc * 8;
   }
+  // the hidden slice has kRows rows: kLoadsH instructions per wave
+  uint32_t voff_h[kLoadsH];
+  int kchunk_h[kLoadsH];
+#pragma unroll
+  for (int j = 0; j < kLoadsH; ++j) {
+    const int r = (wave * kLoadsH + j) * 8 + (lane >> 3);
+    const int cc = (lane & 7) ^ swz(r);
+    voff_h[j] = (uint32_t)r * (uint32_t)H * 2u + (uint32_t)cc * 16u;
+    kchunk_h[j] = cc * 8;
+  }
   const __amdgpu_buffer_rsrc_t rsrc_h = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((const uint16_t*)p.hidden + m0 * H), (short)0, rows_here * H * 2, kRsrcWord3);
 
@@ -204,23 +218,23 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
   for (int uu = 0; uu < 4; ++uu) {
     const int c = (2 * uu + half) ^ fr;
     a_off[uu] = ((wv * 128 + (lane & 31)) * kChunks + c) * 16;
-    b_off[uu] = kTileBytes + ((wt * 64 + (lane & 31)) * kChunks + c) * 16;
+    b_off[uu] = kTileBytes + ((wt * kWaveTok + (lane & 31)) * kChunks + c) * 16;
   }
 
   // ---- targets of this lane's two token columns ------------------------------
-  int64_t tgt[2];
+  int64_t tgt[kTi];
 #pragma unroll
-  for (int ti = 0; ti < 2; ++ti) {
-    const int j = wt * 64 + ti * 32 + (lane & 31);
+  for (int ti = 0; ti < kTi; ++ti) {
+    const int j = wt * kWaveTok + ti * 32 + (lane & 31);
     tgt[ti] = (j < rows_here) ? p.target[m0 + j] : (int64_t)-1;
   }
   // backward: the forward's lse and the coefficients of
   // dZ = p (g_lse - g_logp) + g_logp [v == target] for the lane's two rows
-  float g_lse_row[2] = {0.f, 0.f}, g_coef[2] = {0.f, 0.f}, g_tgt[2] = {0.f, 0.f};
+  float g_lse_row[kTi] = {}, g_coef[kTi] = {}, g_tgt[kTi] = {};
   if constexpr (kGrad) {
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti) {
-      const int j = wt * 64 + ti * 32 + (lane & 31);
+    for (int ti = 0; ti < kTi; ++ti) {
+      const int j = wt * kWaveTok + ti * 32 + (lane & 31);
       if (j < rows_here) {
         const float gl = p.g_logp[m0 + j];
         g_lse_row[ti] = p.lse[m0 + j];
@@ -260,7 +274,7 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
   auto ctx_h = [&](int g, auto sc) {
     const int v = g / KT;
     const int kt = g - v * KT;
-    int dst = kTileBytes + wave * kLoadsPerOperand * 1024;
+    int dst = kTileBytes + wave * kLoadsH * 1024;
     asm volatile("" : "+s"(dst));
     LoadCtx c;
     c.rsrc = rsrc_h;
@@ -269,14 +283,24 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
     c.kend = (g < G) ? H : 0;
     return c;
   };
-  auto load_one = [&](const LoadCtx& c, int j) {
-    const bool ok = (int)(c.k2 / 2u) + kchunk[j] < c.kend;
-    const uint32_t voff = ok ? voff_base[j] + c.k2 : kOutOfRange;
+  // load j of the W slice (is_h false) or of the hidden slice (is_h true)
+  auto load_one = [&](const LoadCtx& c, int j, auto is_h) {
+    int kc;
+    uint32_t vb;
+    if constexpr (decltype(is_h)::value) {
+      kc = kchunk_h[j];
+      vb = voff_h[j];
+    } else {
+      kc = kchunk[j];
+      vb = voff_base[j];
+    }
+    const bool ok = (int)(c.k2 / 2u) + kc < c.kend;
+    const uint32_t voff = ok ? vb + c.k2 : kOutOfRange;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsrc, (lds_void*)(c.dst + j * 1024), 16, voff, 0,
                                              0, 0);
   };
 
-  floatx16 acc[4][2];
+  floatx16 acc[4][kTi];
 
   // Start the accumulators of vocabulary tile v: the tile's bias values, or 0.
   // acc[vi][ti][r] belongs to vocabulary row wv*128 + vi*32 + 8*(r/4) +
@@ -290,48 +314,56 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
         for (int q = 0; q < 4; ++q) {
           const floatx4 bb = *(const floatx4*)(bt + vi * 32 + 8 * q);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[vi][0][4 * q + e] = bb[e];
-            acc[vi][1][4 * q + e] = bb[e];
-          }
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int ti = 0; ti < kTi; ++ti) acc[vi][ti][4 * q + e] = bb[e];
         }
     } else {
 #pragma unroll
       for (int vi = 0; vi < 4; ++vi)
 #pragma unroll
-        for (int ti = 0; ti < 2; ++ti) acc[vi][ti] = floatx16{};
+        for (int ti = 0; ti < kTi; ++ti) acc[vi][ti] = floatx16{};
     }
   };
 
-  // One K step in a fixed instruction order: MFMA i (tile (i/2, i%2)) is
-  // followed by LDS read i of the next step's fragments (i < 6) and, when a
-  // load context is given, by direct load i/2 after every odd MFMA.  The
-  // fences keep the compiler from regrouping: reads must not bunch up behind
-  // their uses, and loads issued in a burst would stall the wave (the
-  // texture-address unit takes one 1 KB load about every 16 cycles) and with
-  // it the MFMAs behind them.
-  auto step = [&](const bf16x8 (&a)[4], const bf16x8 (&b)[2], const uint8_t* nst, int nuu,
-                  bf16x8 (&na)[4], bf16x8 (&nb)[2], const LoadCtx& lc, auto with_loads) {
+  // One K step in a fixed instruction order: MFMA i (tile (i/kTi, i%kTi)) is
+  // followed by the next step's LDS reads (two columns: one read after each
+  // of the first six MFMAs; one column: b0 and a0 after the first, then one)
+  // and, when a load context is given, by its direct loads spread evenly over
+  // the step.  The fences keep the compiler from regrouping: reads must not
+  // bunch up behind their uses, and loads issued in a burst would stall the
+  // wave (the texture-address unit takes one 1 KB load about every 16 cycles)
+  // and with it the MFMAs behind them.
+  auto step = [&](const bf16x8 (&a)[4], const bf16x8 (&b)[kTi], const uint8_t* nst, int nuu,
+                  bf16x8 (&na)[4], bf16x8 (&nb)[kTi], const LoadCtx& lc, auto with_loads,
+                  auto is_h) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int vi = i >> 1, ti = i & 1;
+    for (int i = 0; i < 4 * kTi; ++i) {
+      const int vi = i / kTi, ti = i % kTi;
       acc[vi][ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[vi], b[ti], acc[vi][ti], 0, 0, 0);
-      // next-step fragments in the order the MFMAs need them: b0 a0 b1 a1 a2 a3
-      if (i == 0) nb[0] = *(const bf16x8*)(nst + b_off[nuu]);
-      if (i == 1) na[0] = *(const bf16x8*)(nst + a_off[nuu]);
-      if (i == 2) nb[1] = *(const bf16x8*)(nst + b_off[nuu] + 32 * kLdsRowBytes);
-      if (i >= 3 && i < 6)
-        na[i - 2] = *(const bf16x8*)(nst + a_off[nuu] + (i - 2) * 32 * kLdsRowBytes);
+      if constexpr (kTi == 2) {
+        // next-step fragments in the order the MFMAs need them: b0 a0 b1 a1 a2 a3
+        if (i == 0) nb[0] = *(const bf16x8*)(nst + b_off[nuu]);
+        if (i == 1) na[0] = *(const bf16x8*)(nst + a_off[nuu]);
+        if (i == 2) nb[1] = *(const bf16x8*)(nst + b_off[nuu] + 32 * kLdsRowBytes);
+        if (i >= 3 && i < 6)
+          na[i - 2] = *(const bf16x8*)(nst + a_off[nuu] + (i - 2) * 32 * kLdsRowBytes);
+      } else {
+        if (i == 0) nb[0] = *(const bf16x8*)(nst + b_off[nuu]);
+        na[i] = *(const bf16x8*)(nst + a_off[nuu] + i * 32 * kLdsRowBytes);
+      }
       if constexpr (decltype(with_loads)::value) {
-        if (i & 1) load_one(lc, i >> 1);
+        constexpr int nl = decltype(is_h)::value ? kLoadsH : kLoadsPerOperand;
+        constexpr int stride = 4 * kTi / nl;
+        if (i % stride == stride - 1) load_one(lc, i / stride, is_h);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto read_frags = [&](const uint8_t* st, int uu, bf16x8 (&a)[4], bf16x8 (&b)[2]) {
+  auto read_frags = [&](const uint8_t* st, int uu, bf16x8 (&a)[4], bf16x8 (&b)[kTi]) {
     b[0] = *(const bf16x8*)(st + b_off[uu]);
     a[0] = *(const bf16x8*)(st + a_off[uu]);
-    b[1] = *(const bf16x8*)(st + b_off[uu] + 32 * kLdsRowBytes);
+    if constexpr (kTi == 2) b[1] = *(const bf16x8*)(st + b_off[uu] + 32 * kLdsRowBytes);
 #pragma unroll
     for (int vi = 1; vi < 4; ++vi)
       a[vi] = *(const bf16x8*)(st + a_off[uu] + vi * 32 * kLdsRowBytes);
@@ -347,34 +379,38 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
 
-  bf16x8 fa0[4], fb0[2], fa1[4], fb1[2];
+  bf16x8 fa0[4], fb0[kTi], fa1[4], fb1[kTi];
 
   // Stage g, computed from buffer SC; buffer SN holds stage g + 1.  On entry
   // fa0/fb0 hold step 0 of stage g; on exit they hold step 0 of stage g + 1.
   auto stage = [&](int g, auto sc, auto sn) {
     const uint8_t* st = slot_ptr(sc);
     const LoadCtx lh = ctx_h(g + 1, sn);
-    step(fa0, fb0, st, 1, fa1, fb1, lh, std::true_type{});
-    step(fa1, fb1, st, 2, fa0, fb0, lh, std::false_type{});
-    step(fa0, fb0, st, 3, fa1, fb1, lh, std::false_type{});
+    step(fa0, fb0, st, 1, fa1, fb1, lh, std::true_type{}, std::true_type{});
+    step(fa1, fb1, st, 2, fa0, fb0, lh, std::false_type{}, std::true_type{});
+    step(fa0, fb0, st, 3, fa1, fb1, lh, std::false_type{}, std::true_type{});
     sync_stage();
     const LoadCtx lw = ctx_w(g + 2, sc);
-    step(fa1, fb1, slot_ptr(sn), 0, fa0, fb0, lw, std::true_type{});
+    step(fa1, fb1, slot_ptr(sn), 0, fa0, fb0, lw, std::true_type{}, std::false_type{});
   };
 
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float s_run[2] = {0.f, 0.f};
+  float m_run[kTi], s_run[kTi];
+#pragma unroll
+  for (int ti = 0; ti < kTi; ++ti) {
+    m_run[ti] = -INFINITY;
+    s_run[ti] = 0.f;
+  }
 
   // Prologue: stage 0 whole and the W slice of stage 1 (its hidden slice is
   // issued in stage 0).
   {
     const LoadCtx w0 = ctx_w(0, Slot<0>{}), h0 = ctx_h(0, Slot<0>{}), w1 = ctx_w(1, Slot<1>{});
 #pragma unroll
-    for (int j = 0; j < kLoadsPerOperand; ++j) load_one(w0, j);
+    for (int j = 0; j < kLoadsPerOperand; ++j) load_one(w0, j, std::false_type{});
 #pragma unroll
-    for (int j = 0; j < kLoadsPerOperand; ++j) load_one(h0, j);
+    for (int j = 0; j < kLoadsH; ++j) load_one(h0, j, std::true_type{});
 #pragma unroll
-    for (int j = 0; j < kLoadsPerOperand; ++j) load_one(w1, j);
+    for (int j = 0; j < kLoadsPerOperand; ++j) load_one(w1, j, std::false_type{});
   }
   init_acc(0);
   wait_vmcnt<0>();
@@ -403,12 +439,12 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
           (void*)(p.dzt + (int64_t)vbase * p.ldz), (short)0, vrows * (int)p.ldz * 2, kRsrcWord3);
       // per token column: its row, whether it exists, the store offset and
       // the target's (vi, r) offset relative to this lane's first column
-      uint32_t vo[2];
-      bool live[2];
-      int64_t trel[2];
+      uint32_t vo[kTi];
+      bool live[kTi];
+      int64_t trel[kTi];
 #pragma unroll
-      for (int ti = 0; ti < 2; ++ti) {
-        const int jr = wt * 64 + ti * 32 + (lane & 31);
+      for (int ti = 0; ti < kTi; ++ti) {
+        const int jr = wt * kWaveTok + ti * 32 + (lane & 31);
         live[ti] = jr < rows_here;
         vo[ti] = ((uint32_t)(wv * 128 + 4 * half) * (uint32_t)p.ldz + (uint32_t)(m0 + jr)) * 2u;
         // opaque per tile: the store addresses are formed here, not hoisted
@@ -426,7 +462,7 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
         for (int r = 0; r < 16; ++r) {
           const int k = vi * 32 + 8 * (r >> 2) + (r & 3);      // column - vw - 4 half
 #pragma unroll
-          for (int ti = 0; ti < 2; ++ti) {
+          for (int ti = 0; ti < kTi; ++ti) {
             float dz = exp2_hw((acc[vi][ti][r] - g_lse_row[ti]) * kLog2e) * g_coef[ti];
             if (trel[ti] == k) dz += g_tgt[ti];
             if (live[ti])
@@ -446,14 +482,14 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
         for (int r = 0; r < 16; ++r) {
           const int col = vw + vi * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
           if (col >= p.V) {
-            acc[vi][0][r] = -INFINITY;
-            acc[vi][1][r] = -INFINITY;
+#pragma unroll
+            for (int ti = 0; ti < kTi; ++ti) acc[vi][ti][r] = -INFINITY;
           }
         }
     }
 
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti) {
+    for (int ti = 0; ti < kTi; ++ti) {
       // target capture: exactly one (tile, lane, register) in the grid holds it
       const int64_t rel64 = tgt[ti] - vw;
       const int rel = (int)rel64;
@@ -467,7 +503,7 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             if (vi == vi_t && r == r_t) val = acc[vi][ti][r];
-        if (hit) p.tlogit[m0 + wt * 64 + ti * 32 + (lane & 31)] = val;
+        if (hit) p.tlogit[m0 + wt * kWaveTok + ti * 32 + (lane & 31)] = val;
       }
 
       // online softmax over this lane's 64 values of the tile
@@ -497,9 +533,9 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
   if constexpr (kGrad) return;
 
   // ---- split done: merge lane halves, then the two vocabulary-half waves ----
-  float mm[2], ss[2];
+  float mm[kTi], ss[kTi];
 #pragma unroll
-  for (int ti = 0; ti < 2; ++ti) {
+  for (int ti = 0; ti < kTi; ++ti) {
     const float om = __shfl_xor(m_run[ti], 32);
     const float os = __shfl_xor(s_run[ti], 32);
     if (half == 0)
@@ -509,13 +545,13 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
   }
   if (wv == 1 && half == 0) {
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti) red[wt * 64 + ti * 32 + lane] = make_float2(mm[ti], ss[ti]);
+    for (int ti = 0; ti < kTi; ++ti) red[wt * kWaveTok + ti * 32 + lane] = make_float2(mm[ti], ss[ti]);
   }
   __syncthreads();
   if (wv == 0 && half == 0) {
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti) {
-      const int j = wt * 64 + ti * 32 + lane;
+    for (int ti = 0; ti < kTi; ++ti) {
+      const int j = wt * kWaveTok + ti * 32 + lane;
       const float2 hi = red[j];
       float m, s;
       merge_state(mm[ti], ss[ti], hi.x, hi.y, m, s);
@@ -525,16 +561,30 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
 }
 
 __global__ __launch_bounds__(kThreads, 1) void proj_lse_kernel(const ProjParams p) {
-  proj_lse_body<false, false>(p);
+  proj_lse_body<false, false, 2>(p);
 }
 __global__ __launch_bounds__(kThreads, 1) void proj_lse_bias_kernel(const ProjParams p) {
-  proj_lse_body<true, false>(p);
+  proj_lse_body<true, false, 2>(p);
 }
 __global__ __launch_bounds__(kThreads, 1) void softmax_grad_kernel(const ProjParams p) {
-  proj_lse_body<false, true>(p);
+  proj_lse_body<false, true, 2>(p);
 }
 __global__ __launch_bounds__(kThreads, 1) void softmax_grad_bias_kernel(const ProjParams p) {
-  proj_lse_body<true, true>(p);
+  proj_lse_body<true, true, 2>(p);
+}
+// 128-token row blocks: twice the workgroups for batches that 256-token
+// blocks cannot spread over every compute unit; the same bits
+__global__ __launch_bounds__(kThreads, 1) void proj_lse_r128_kernel(const ProjParams p) {
+  proj_lse_body<false, false, 1>(p);
+}
+__global__ __launch_bounds__(kThreads, 1) void proj_lse_bias_r128_kernel(const ProjParams p) {
+  proj_lse_body<true, false, 1>(p);
+}
+__global__ __launch_bounds__(kThreads, 1) void softmax_grad_r128_kernel(const ProjParams p) {
+  proj_lse_body<false, true, 1>(p);
+}
+__global__ __launch_bounds__(kThreads, 1) void softmax_grad_bias_r128_kernel(const ProjParams p) {
+  proj_lse_body<true, true, 1>(p);
 }
 
 // Zero columns [N, ldz) of every row of dZ^T (the padding the GEMMs read).
@@ -591,11 +641,10 @@ hipError_t launch_bias_f32(const void* bias, int32_t kind, int32_t V, float* out
 hipError_t launch_softmax_grad(const ProjParams& p, hipStream_t stream) {
   const int64_t blocks = (int64_t)p.R * p.S_grid;
   if (blocks <= 0) return hipSuccess;
-  if (p.bias_kind != kBiasNone)
-    hipLaunchKernelGGL(softmax_grad_bias_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
-                       stream, p);
-  else
-    hipLaunchKernelGGL(softmax_grad_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  const bool bias = p.bias_kind != kBiasNone;
+  auto k = p.rows == 128 ? (bias ? softmax_grad_bias_r128_kernel : softmax_grad_r128_kernel)
+                         : (bias ? softmax_grad_bias_kernel : softmax_grad_kernel);
+  hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -619,10 +668,10 @@ hipError_t launch_row_sums(const uint16_t* dzt, int64_t rows, int64_t N, int64_t
 hipError_t launch_proj_lse(const ProjParams& p, hipStream_t stream) {
   const int64_t blocks = (int64_t)p.R * p.S_grid;
   if (blocks <= 0) return hipSuccess;
-  if (p.bias_kind != kBiasNone)
-    hipLaunchKernelGGL(proj_lse_bias_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(proj_lse_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  const bool bias = p.bias_kind != kBiasNone;
+  auto k = p.rows == 128 ? (bias ? proj_lse_bias_r128_kernel : proj_lse_r128_kernel)
+                         : (bias ? proj_lse_bias_kernel : proj_lse_kernel);
+  hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

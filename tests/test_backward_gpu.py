@@ -176,13 +176,17 @@ def test_empty_batch_zero_weight_gradient():
     assert torch.equal(gb, torch.zeros_like(gb))
 
 
-@pytest.mark.parametrize("chunk", [1, 7, 256, 300])
-def test_grad_hidden_rows_do_not_depend_on_the_batch(chunk):
+@pytest.mark.parametrize("N,H,V,chunk", [
+    (700, 512, 2100, 1), (700, 512, 2100, 7), (700, 512, 2100, 256), (700, 512, 2100, 300),
+    # 64 splits: the full batch runs 256-token row blocks (5 x 64 workgroups), the
+    # chunks 128-token blocks (at most 3 x 64 < 256 compute units)
+    (1100, 256, 16384, 300), (1100, 256, 16384, 37),
+])
+def test_grad_hidden_rows_do_not_depend_on_the_batch(N, H, V, chunk):
     """grad_hidden of a row is the same bits in any batch: chunked calls and a
     permuted batch reproduce the full batch's rows exactly."""
-    N, H, V = 700, 512, 2100
     inp, up = _inputs(N, H, V, 8, "bf16")
-    say(f"grad_hidden batch invariance chunk={chunk}")
+    say(f"grad_hidden batch invariance N={N} V={V} chunk={chunk}")
     with torch.no_grad():
         _, lse = ila.forward(inp["hidden"], inp["weight"], inp["target"], inp["bias"])
     full, _, _, _ = _run(inp, up, lse)

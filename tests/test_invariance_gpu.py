@@ -4,6 +4,9 @@ not depend on its slot, its neighbours, the tensor layout, the stream or the
 run.  RL-Kernel PR #337, description (tests paragraph and "What this PR
 changes"): same row + same V -> same arithmetic order and bits; the
 annotation on the chunk test: full-batch bits equal concatenated chunk bits.
+The sweep workload's full batch runs 256-token row blocks and its chunks of up
+to 1000 rows 128-token blocks (too few 256-token blocks to fill the device),
+so the chunk comparison also holds the two block heights to the same bits.
 """
 
 import pytest
