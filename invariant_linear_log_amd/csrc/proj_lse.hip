@@ -7,7 +7,8 @@
 // per-row online-softmax partial (running max m, sum s of exp(z - m)).  The
 // partials are merged by merge.hip.
 //
-// Workgroup: 512 threads (8 wave64s), one (row block of 256 tokens, split).
+// Workgroup: 512 threads (8 wave64s), one (row block of 256 tokens, split)
+// (or 128 tokens, below).
 // Per vocabulary tile of 256 columns the workgroup computes the 256 x 256
 // product W_tile[256, H] . hidden_block[256, H]^T with
 // v_mfma_f32_32x32x16_bf16, W as the A operand (MFMA rows = vocabulary) and
@@ -19,6 +20,10 @@
 // Waves: w = 2 * wt + wv.  wv in {0, 1} picks vocabulary rows [128 wv, +128)
 // of the tile, wt in {0..3} picks tokens [64 wt, +64) of the block.  A wave
 // holds 4 x 2 MFMA tiles of 32 x 32 (128 accumulator registers per lane).
+// A second instantiation takes 128-token row blocks (tokens [32 wt, +32), 4 x
+// 1 MFMA tiles per wave) for batches too small to give every compute unit a
+// 256-token block; the vocabulary side, and with it each token's arithmetic,
+// is the same in both.
 //
 // Bit contract.  For a fixed (token, vocabulary column) the K reduction is
 // the same chain of MFMA instructions over ascending 16-wide K steps
@@ -182,10 +187,10 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
   const int KT = ((H + kBK - 1) / kBK + 1) / 2 * 2;
   const int G = nvt * KT;                          // stages in this workgroup
 
-  // ---- per-lane load descriptors: 4 + 4 direct-to-LDS loads per stage ------
+  // ---- per-lane load descriptors: 4 + kLoadsH direct-to-LDS loads per stage --
   // Instruction j of wave `wave` fills chunk slots [(4 wave + j) * 64, +64) of
-  // the W slice and of the hidden slice: 8 rows x 8 chunks of 16 bytes, i.e.
-  // eight whole 128-byte lines.
+  // the W slice (and [(kLoadsH wave + j) * 64, +64) of the hidden slice): 8
+  // rows x 8 chunks of 16 bytes, i.e. eight whole 128-byte lines.
   uint32_t voff_base[kLoadsPerOperand];
   int kchunk[kLoadsPerOperand];
 #pragma unroll
@@ -210,7 +215,7 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
 
   // ---- per-lane LDS read offsets for the MFMA operands ----------------------
   // A (W): row wv*128 + vi*32 + (lane & 31), K chunk 2u + half; vi adds 4 KB.
-  // B (hidden): row wt*64 + ti*32 + (lane & 31); ti adds 4 KB.  The swizzle
+  // B (hidden): row wt*kWaveTok + ti*32 + (lane & 31); ti adds 4 KB.  The swizzle
   // only reads row bits 1-3, which come from the lane.
   const int fr = swz(lane & 31);
   int a_off[4], b_off[4];
@@ -221,7 +226,7 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
     b_off[uu] = kTileBytes + ((wt * kWaveTok + (lane & 31)) * kChunks + c) * 16;
   }
 
-  // ---- targets of this lane's two token columns ------------------------------
+  // ---- targets of this lane's token columns (kTi of them) -------------------
   int64_t tgt[kTi];
 #pragma unroll
   for (int ti = 0; ti < kTi; ++ti) {
@@ -229,7 +234,7 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
     tgt[ti] = (j < rows_here) ? p.target[m0 + j] : (int64_t)-1;
   }
   // backward: the forward's lse and the coefficients of
-  // dZ = p (g_lse - g_logp) + g_logp [v == target] for the lane's two rows
+  // dZ = p (g_lse - g_logp) + g_logp [v == target] for the lane's rows
   float g_lse_row[kTi] = {}, g_coef[kTi] = {}, g_tgt[kTi] = {};
   if constexpr (kGrad) {
 #pragma unroll
@@ -426,7 +431,7 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
     if (g + 2 != (v + 1) * KT) continue;
 
     // ---- epilogue of vocabulary tile v -------------------------------------
-    // acc[vi][ti][r] holds z for token column wt*64 + ti*32 + (lane & 31) and
+    // acc[vi][ti][r] holds z for token column wt*kWaveTok + ti*32 + (lane & 31) and
     // vocabulary row wv*128 + vi*32 + 8*(r/4) + 4*half + (r%4) of the tile.
     const int vbase = (vt_begin + v) * kVtileCols;
     const int vw = vbase + wv * 128;               // first column of this wave
