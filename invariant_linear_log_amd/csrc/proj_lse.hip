@@ -57,10 +57,9 @@
 // instruction, with its MFMAs queued behind it, until the unit drained.
 // Interleaved, the loads drain while the matrix cores work.
 //
-// Bias.  Each logit's accumulation starts from its bias value (fp32, from
-// the padded copy the host library prepares), loaded straight into the
-// accumulator registers when a vocabulary tile starts; the K products are
-// then added in ascending order.  Without bias the accumulators start at 0.
+// Bias.  Each logit is the fp32 K accumulation (started at 0) plus its bias
+// value, added once in the tile epilogue (fp32, from the padded copy the host
+// library prepares, staged through LDS one tile ahead).
 //
 // LDS layout.  Each 256 x 64 slice is 256 rows of eight 16-byte chunks,
 // chunk c of row r stored at position c ^ f(r), f(r) = (r >> 1) & 7.
@@ -148,6 +147,8 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
   __shared__ __attribute__((aligned(1024))) uint8_t slot0[kSlotBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t slot1[kSlotBytes];
   __shared__ float2 red[kBlockRows];
+  // bias of the current and the next vocabulary tile (bias kernels only)
+  __shared__ __attribute__((aligned(16))) float bias_lds[2][kVtileCols];
 
   auto slot_ptr = [&](auto sc) -> uint8_t* {
     if constexpr (decltype(sc)::value == 0) return slot0;
@@ -227,11 +228,12 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
   }
 
   // ---- targets of this lane's token columns (kTi of them) -------------------
-  int64_t tgt[kTi];
+  int tgt[kTi];          // the target, or -1 when outside [0, V) (V <= 2^30)
 #pragma unroll
   for (int ti = 0; ti < kTi; ++ti) {
     const int j = wt * kWaveTok + ti * 32 + (lane & 31);
-    tgt[ti] = (j < rows_here) ? p.target[m0 + j] : (int64_t)-1;
+    const int64_t t = (j < rows_here) ? p.target[m0 + j] : (int64_t)-1;
+    tgt[ti] = (t >= 0 && t < p.V) ? (int)t : -1;
   }
   // backward: the forward's lse and the coefficients of
   // dZ = p (g_lse - g_logp) + g_logp [v == target] for the lane's rows
@@ -310,25 +312,29 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
   // Start the accumulators of vocabulary tile v: the tile's bias values, or 0.
   // acc[vi][ti][r] belongs to vocabulary row wv*128 + vi*32 + 8*(r/4) +
   // 4*half + (r%4) of the tile (for both token columns ti).
-  auto init_acc = [&](int v) {
-    if (kHasBias && v < nvt) {
-      const float* bt = (const float*)p.bias + (vt_begin + v) * kVtileCols + wv * 128 + 4 * half;
-#pragma unroll
-      for (int vi = 0; vi < 4; ++vi)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const floatx4 bb = *(const floatx4*)(bt + vi * 32 + 8 * q);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int ti = 0; ti < kTi; ++ti) acc[vi][ti][4 * q + e] = bb[e];
-        }
-    } else {
-#pragma unroll
-      for (int vi = 0; vi < 4; ++vi)
-#pragma unroll
-        for (int ti = 0; ti < kTi; ++ti) acc[vi][ti] = floatx16{};
+  // The bias of tile v reaches LDS (bias_lds[v & 1]) by one direct load of
+  // 1 KB from wave 0, issued in the epilogue of tile v - 1 once that tile's
+  // bias is consumed (tile 0: in the prologue); tile v's first stage barrier
+  // makes it visible.  The epilogue of tile v reads it from there: nothing
+  // bias-related runs in the stage loop, and no global load whose wait would
+  // also wait for the next stages' prefetch (the load counter is in order).
+  const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const float*)p.bias + (int64_t)vt_begin * kVtileCols), (short)0,
+      kHasBias ? nvt * kVtileCols * 4 : 0, kRsrcWord3);     // unused without bias
+  auto load_bias = [&](int v) {
+    if constexpr (kHasBias) {
+      if (wave == 0 && v < nvt)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_b, (lds_void*)&bias_lds[v & 1][0], 16,
+                                                 (uint32_t)v * 1024u + (uint32_t)lane * 16u, 0, 0,
+                                                 0);
     }
+  };
+  // Every tile's accumulators start at 0.
+  auto init_acc = [&](int) {
+#pragma unroll
+    for (int vi = 0; vi < 4; ++vi)
+#pragma unroll
+      for (int ti = 0; ti < kTi; ++ti) acc[vi][ti] = floatx16{};
   };
 
   // One K step in a fixed instruction order: MFMA i (tile (i/kTi, i%kTi)) is
@@ -416,10 +422,11 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
     for (int j = 0; j < kLoadsH; ++j) load_one(h0, j, std::true_type{});
 #pragma unroll
     for (int j = 0; j < kLoadsPerOperand; ++j) load_one(w1, j, std::false_type{});
+    load_bias(0);
   }
-  init_acc(0);
   wait_vmcnt<0>();
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  init_acc(0);
   read_frags(slot0, 0, fa0, fb0);
 
   // G is even: stage g lives in buffer 0, stage g + 1 in buffer 1.
@@ -435,6 +442,24 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
     // vocabulary row wv*128 + vi*32 + 8*(r/4) + 4*half + (r%4) of the tile.
     const int vbase = (vt_begin + v) * kVtileCols;
     const int vw = vbase + wv * 128;               // first column of this wave
+    if constexpr (kHasBias) {
+      // z = (the K accumulation) + bias: one fp32 add per logit
+      __builtin_amdgcn_sched_barrier(0);
+      const float* bt = &bias_lds[v & 1][wv * 128 + 4 * half];
+#pragma unroll
+      for (int vi = 0; vi < 4; ++vi) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const floatx4 bb = *(const floatx4*)(bt + vi * 32 + 8 * q);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int ti = 0; ti < kTi; ++ti) acc[vi][ti][4 * q + e] += bb[e];
+        }
+        __builtin_amdgcn_sched_barrier(0);        // a few bias values live at a time
+      }
+      load_bias(v + 1);          // lands during the next tile's first stage
+    }
     if constexpr (kGrad) {
       // dZ^T[col][row] = p (g_lse - g_logp) + g_logp [col == target], p =
       // exp(z - lse): 32 consecutive rows per store (coalesced).  The buffer
@@ -446,7 +471,7 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
       // the target's (vi, r) offset relative to this lane's first column
       uint32_t vo[kTi];
       bool live[kTi];
-      int64_t trel[kTi];
+      int trel[kTi];
 #pragma unroll
       for (int ti = 0; ti < kTi; ++ti) {
         const int jr = wt * kWaveTok + ti * 32 + (lane & 31);
@@ -496,7 +521,7 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
 #pragma unroll
     for (int ti = 0; ti < kTi; ++ti) {
       // target capture: exactly one (tile, lane, register) in the grid holds it
-      const int64_t rel64 = tgt[ti] - vw;
+      const int rel64 = tgt[ti] - vw;
       const int rel = (int)rel64;
       const bool hit = rel64 >= 0 && rel64 < 128 && ((rel >> 2) & 1) == half;
       if (__any(hit)) {
@@ -528,6 +553,7 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
       s_run[ti] = s_run[ti] * exp2_hw((m_run[ti] - mu) * kLog2e) + tile_sum;
       m_run[ti] = m_new;
     }
+    __builtin_amdgcn_sched_barrier(0);      // the tile is consumed before the next one starts
     init_acc(v + 1);
   }
 

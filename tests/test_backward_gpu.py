@@ -222,15 +222,16 @@ def test_run_to_run_and_streams():
         assert torch.equal(x, y)
 
 
-def test_autograd_linear_logp():
+@pytest.mark.parametrize("bias", ["f32", "bf16"])
+def test_autograd_linear_logp(bias):
     """linear_logp: the forward's outputs, and gradients equal to backward()'s
     (rounded once to the inputs' dtypes)."""
     N, H, V = 300, 256, 1200
-    inp, up = _inputs(N, H, V, 10, "f32")
+    inp, up = _inputs(N, H, V, 10, bias)
     h = inp["hidden"].clone().requires_grad_(True)
     w = inp["weight"].clone().requires_grad_(True)
     b = inp["bias"].clone().requires_grad_(True)
-    say("linear_logp autograd")
+    say(f"linear_logp autograd, {bias} bias")
     logp, lse = ila.linear_logp(h, w, inp["target"], b)
     (logp * up["grad_logp"] + lse * up["grad_lse"]).sum().backward()
     with torch.no_grad():
@@ -241,7 +242,25 @@ def test_autograd_linear_logp():
     assert torch.equal(logp, ref_logp) and torch.equal(lse, ref_lse)
     assert torch.equal(h.grad, gh.to(torch.bfloat16))
     assert torch.equal(w.grad, gw.to(torch.bfloat16))
-    assert torch.equal(b.grad, gb)
+    assert b.grad.dtype == b.dtype and torch.equal(b.grad, gb.to(b.dtype))
+
+
+def test_autograd_partial_requires_grad():
+    """Only hidden requires grad (a frozen lm-head): the weight and bias get no
+    gradient, and hidden's equals backward()'s."""
+    N, H, V = 200, 128, 900
+    inp, up = _inputs(N, H, V, 11, "f32")
+    h = inp["hidden"].clone().requires_grad_(True)
+    say("linear_logp autograd, frozen weight")
+    logp, lse = ila.linear_logp(h, inp["weight"], inp["target"], inp["bias"])
+    (logp * up["grad_logp"] + lse * up["grad_lse"]).sum().backward()
+    with torch.no_grad():
+        _, ref_lse = ila.forward(inp["hidden"], inp["weight"], inp["target"], inp["bias"])
+        gh, _, _ = ila.backward(inp["hidden"], inp["weight"], inp["target"], inp["bias"],
+                                ref_lse, up["grad_logp"], up["grad_lse"])
+    torch.cuda.synchronize()
+    assert torch.equal(h.grad, gh.to(torch.bfloat16))
+    assert inp["weight"].grad is None and inp["bias"].grad is None
 
 
 def test_headline_sampled_parity():
