@@ -106,15 +106,15 @@ def measured_traffic(workload):
 
 def invariance_cost(h, t, w, b, steps=10, warmup=3):
     """ms per full forward step under the invariant and the throughput split
-    policies, at the workload's N and at its first 512 rows (fewer row blocks:
-    the throughput policy then adds splits to fill the device)."""
+    policies, at the workload's N and at its first 512 and 64 rows (fewer row
+    blocks: the throughput policy then adds splits to fill the device)."""
     import torch
     import invariant_linear_log_amd as ila
     dev = h.device
     cu = ila.device_cu_count(dev)
     stream = torch.cuda.Stream(device=dev)
     res = {"cu_count": cu}
-    for n in (h.shape[0], 512):
+    for n in (h.shape[0], 512, 64):
         hn, tn = h[:n].contiguous(), t[:n].contiguous()
         V = w.shape[0]
         logp = torch.empty(n, dtype=torch.float32, device=dev)
