@@ -252,7 +252,7 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
   }
 
   // Direct-to-LDS loads of stage g into buffer SC, one instruction at a
-  // time: load j (0..3) of the W slice or of the hidden slice.  A stage past
+  // time: load j of the W slice (0..3) or of the hidden slice (0..kLoadsH-1).  A stage past
   // the end (g >= G) reads nothing (empty range) and writes zeros into a
   // buffer that is no longer read; no branch, so the loads can sit between
   // MFMAs.
@@ -307,11 +307,10 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
                                              0, 0);
   };
 
+  // acc[vi][ti][r] belongs to vocabulary row wv*128 + vi*32 + 8*(r/4) +
+  // 4*half + (r%4) of the tile (for every token column ti).
   floatx16 acc[4][kTi];
 
-  // Start the accumulators of vocabulary tile v: the tile's bias values, or 0.
-  // acc[vi][ti][r] belongs to vocabulary row wv*128 + vi*32 + 8*(r/4) +
-  // 4*half + (r%4) of the tile (for both token columns ti).
   // The bias of tile v reaches LDS (bias_lds[v & 1]) by one direct load of
   // 1 KB from wave 0, issued in the epilogue of tile v - 1 once that tile's
   // bias is consumed (tile 0: in the prologue); tile v's first stage barrier
@@ -521,9 +520,8 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
 #pragma unroll
     for (int ti = 0; ti < kTi; ++ti) {
       // target capture: exactly one (tile, lane, register) in the grid holds it
-      const int rel64 = tgt[ti] - vw;
-      const int rel = (int)rel64;
-      const bool hit = rel64 >= 0 && rel64 < 128 && ((rel >> 2) & 1) == half;
+      const int rel = tgt[ti] - vw;
+      const bool hit = rel >= 0 && rel < 128 && ((rel >> 2) & 1) == half;
       if (__any(hit)) {
         const int vi_t = rel >> 5;
         const int r_t = ((rel >> 3) & 3) * 4 + (rel & 3);
