@@ -515,6 +515,7 @@ bilogp_status gemm_run(const GemmCall& c, int64_t M, int64_t N, int64_t K, void*
   g.out_kind = c.out_kind;
   g.Pt = (int32_t)((c.P + 255) / 256);
   g.Qt = (int32_t)((c.Q + 255) / 256);
+  g.cu_count = g_cu_count[dev].load(std::memory_order_acquire);
   if ((int64_t)g.Pt * g.Qt > INT32_MAX) return fail(BILOGP_E_INVALID_ARG, "too many tiles");
   hipError_t e = bilogp::launch_det_gemm(g, c.xt, c.yt, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(BILOGP_E_HIP, std::string("gemm launch: ") + hipGetErrorString(e));
@@ -678,6 +679,7 @@ bilogp_status bilogp_backward(const void* hidden, const void* weight, const int6
       g.x = weight; g.y = dzt; g.out = grad_hidden;
       g.P = H; g.Q = N; g.C = V; g.ldx = H; g.ldy = ldz; g.ldo = H;
       g.out_kind = bilogp::kGemmF32;
+      g.cu_count = g_cu_count[dev].load(std::memory_order_acquire);
       g.Pt = (int32_t)((H + 255) / 256);
       g.Qt = (int32_t)((N + 255) / 256);
       e = bilogp::launch_det_gemm(g, true, true, s);
@@ -689,6 +691,7 @@ bilogp_status bilogp_backward(const void* hidden, const void* weight, const int6
     g.x = hidden; g.y = dzt; g.out = grad_weight;
     g.P = H; g.Q = V; g.C = N; g.ldx = H; g.ldy = ldz; g.ldo = H;
     g.out_kind = bilogp::kGemmF32;
+    g.cu_count = g_cu_count[dev].load(std::memory_order_acquire);
     g.Pt = (int32_t)((H + 255) / 256);
     g.Qt = (int32_t)((V + 255) / 256);
     e = bilogp::launch_det_gemm(g, true, false, s);

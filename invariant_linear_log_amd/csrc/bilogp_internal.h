@@ -90,7 +90,8 @@ struct GemmParams {
   int64_t P, Q, C;
   int64_t ldx, ldy, ldo;   // row pitches in elements
   int32_t out_kind;        // GemmOut
-  int32_t Pt, Qt;          // 256-wide tiles along P and Q
+  int32_t Pt, Qt;          // tiles along P and Q (set by launch_det_gemm)
+  int32_t cu_count;        // compute units of the device (tile-size choice), 0 unknown
 };
 
 enum GemmOut : int32_t { kGemmBf16 = 0, kGemmF32 = 1, kGemmF32Accum = 2 };

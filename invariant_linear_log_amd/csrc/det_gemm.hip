@@ -65,16 +65,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) short4v lds_short4;
 
 constexpr int kThreads = 256;
-constexpr int kTile = 256;                          // D tile: 256 rows p x 256 columns q
 constexpr int kBK = 64;                             // contraction per stage
-constexpr int kOpBytes = kTile * kBK * 2;           // 32 KB: one operand slice
-constexpr int kSlotBytes = 2 * kOpBytes;            // X slice, Y slice
-constexpr int kLoads = kOpBytes / (kThreads * 16);  // 8 loads per thread and operand
 constexpr int kTileGroup = 4;                       // q tiles per tile-order group
 constexpr uint32_t kOutOfRange = 0x7ffffff0u;
 constexpr int kRsrcWord3 = 0x00020000;
 
-static_assert(kLoads == 8, "load mapping assumes 8 instructions per operand");
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -104,8 +99,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base,
                                            kRsrcWord3);
 }
 
-template <bool kXT, bool kYT>
+// kT: the edge of the square D tile (256, or 128 for grids too small to give
+// every compute unit a 256 x 256 tile); each of the 4 waves computes a
+// kT/2 x kT/2 quarter.  The tile size orders and groups the work only: every
+// output is the same MFMA chain in both.
+template <bool kXT, bool kYT, int kT>
 __device__ __forceinline__ void det_gemm_body(const GemmParams& g) {
+  static_assert(kT == 256 || kT == 128, "tile edge");
+  constexpr int kOpBytes = kT * kBK * 2;            // one operand slice: 32 or 16 KB
+  constexpr int kSlotBytes = 2 * kOpBytes;          // X slice, Y slice
+  constexpr int kLoads = kOpBytes / (kThreads * 16);  // loads per thread and operand: 8 or 4
+  constexpr int kHalf = kT / 2;                     // wave tile edge
+  constexpr int kNF = kT / 64;                      // 32-wide MFMA tiles per wave edge
+  constexpr int kRowB = kT * 2;                     // bytes per row of a transposed slice
+  constexpr int kChunksT = kT / 8;                  // 16-byte chunks per transposed row
+  constexpr int kRowsPerLoad = 64 / kChunksT;       // transposed rows per load instruction
   __shared__ __attribute__((aligned(1024))) uint8_t slot0[kSlotBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t slot1[kSlotBytes];
 
@@ -133,8 +141,8 @@ __device__ __forceinline__ void det_gemm_body(const GemmParams& g) {
   const int group_qts = min(g.Qt - first_qt, kTileGroup);
   const int qt = first_qt + (u % in_group) % group_qts;
   const int pt = (u % in_group) / group_qts;
-  const int64_t p0 = (int64_t)pt * kTile;
-  const int64_t q0 = (int64_t)qt * kTile;
+  const int64_t p0 = (int64_t)pt * kT;
+  const int64_t q0 = (int64_t)qt * kT;
   const int64_t C = g.C;
   const int KT = (int)(((C + kBK - 1) / kBK + 1) / 2 * 2);   // even: stage g in buffer g % 2
 
@@ -146,7 +154,7 @@ __device__ __forceinline__ void det_gemm_body(const GemmParams& g) {
   int rowc_chunk[kLoads];
   uint32_t rowc_off[kLoads];
   auto setup_rows = [&](const void* base, int64_t ld, int64_t row0, int64_t nrows) {
-    const int64_t valid = nrows - row0 < kTile ? nrows - row0 : kTile;
+    const int64_t valid = nrows - row0 < kT ? nrows - row0 : kT;
     const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(
         (const uint16_t*)base + row0 * ld, (int)(valid > 0 ? valid * ld * 2 : 0));
 #pragma unroll
@@ -158,17 +166,17 @@ __device__ __forceinline__ void det_gemm_body(const GemmParams& g) {
     }
     return rs;
   };
-  // Transposed operand (64 contraction rows x 256 columns per stage): load j
-  // of wave w fills LDS rows 2 (8 w + j) and 2 (8 w + j) + 1, lane i taking
-  // row 2 (8 w + j) + i / 32 and chunk (i % 32) ^ (4 * (row & 3)).  The
-  // resource is rebuilt per stage (rows c0 .. c0 + 63); columns past the
-  // operand's width read as zero.
+  // Transposed operand (64 contraction rows x kT columns per stage): load j
+  // of wave w fills kRowsPerLoad LDS rows from kRowsPerLoad (kLoads w + j),
+  // lane i taking row kRowsPerLoad (kLoads w + j) + i / kChunksT and chunk
+  // (i % kChunksT) ^ (4 * (row & 3)).  The resource is rebuilt per stage (rows
+  // c0 .. c0 + 63); columns past the operand's width read as zero.
   uint32_t colt_off[kLoads];
   auto setup_cols = [&](int64_t ld, int64_t col0, int64_t ncols) {
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
-      const int row = 2 * (wave * kLoads + j) + (lane >> 5);
-      const int chunk = (lane & 31) ^ (4 * (row & 3));
+      const int row = kRowsPerLoad * (wave * kLoads + j) + lane / kChunksT;
+      const int chunk = (lane % kChunksT) ^ (4 * (row & 3));
       const int64_t col = col0 + chunk * 8;
       colt_off[j] = col < ncols ? (uint32_t)row * (uint32_t)ld * 2u + (uint32_t)col * 2u
                                 : kOutOfRange;
@@ -257,22 +265,22 @@ __device__ __forceinline__ void det_gemm_body(const GemmParams& g) {
   auto tr_off = [&](int sub) {                          // sub: multiple of 32
     const int chunk = (sub + 16 * (gg & 1)) / 8 + ((i16 & 3) >> 1);
     const int pos = chunk ^ (4 * (trow & 3));
-    return trow * 512 + pos * 16 + 8 * (i16 & 1);
+    return trow * kRowB + pos * 16 + 8 * (i16 & 1);
   };
-  int xoff[4], yoff[4];
+  int xoff[kNF], yoff[kNF];
 #pragma unroll
-  for (int vi = 0; vi < 4; ++vi)
-    xoff[vi] = kXT ? tr_off(wv * 128 + vi * 32) : ((wv * 128 + vi * 32) * 8) * 16;
+  for (int vi = 0; vi < kNF; ++vi)
+    xoff[vi] = kXT ? tr_off(wv * kHalf + vi * 32) : ((wv * kHalf + vi * 32) * 8) * 16;
 #pragma unroll
-  for (int ti = 0; ti < 4; ++ti)
-    yoff[ti] = kOpBytes + (kYT ? tr_off(wt * 128 + ti * 32) : ((wt * 128 + ti * 32) * 8) * 16);
+  for (int ti = 0; ti < kNF; ++ti)
+    yoff[ti] = kOpBytes + (kYT ? tr_off(wt * kHalf + ti * 32) : ((wt * kHalf + ti * 32) * 8) * 16);
 
   auto frag = [&](const uint8_t* st, int off, int uu, auto trc) -> bf16x8 {
     if constexpr (decltype(trc)::value) {
       const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_short4*)(st + off + uu * 16 * 512));
+          (lds_short4*)(st + off + uu * 16 * kRowB));
       const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_short4*)(st + off + uu * 16 * 512 + 4 * 512));
+          (lds_short4*)(st + off + uu * 16 * kRowB + 4 * kRowB));
       typedef short short8v __attribute__((ext_vector_type(8)));
       const short8v v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       return __builtin_bit_cast(bf16x8, v);
@@ -281,36 +289,38 @@ __device__ __forceinline__ void det_gemm_body(const GemmParams& g) {
     }
   };
 
-  floatx16 acc[4][4];
+  floatx16 acc[kNF][kNF];
 #pragma unroll
-  for (int vi = 0; vi < 4; ++vi)
+  for (int vi = 0; vi < kNF; ++vi)
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti) acc[vi][ti] = floatx16{};
+    for (int ti = 0; ti < kNF; ++ti) acc[vi][ti] = floatx16{};
 
-  // One K step in fixed order: MFMA i = (vi, ti) = (i / 4, i % 4), then for
-  // i < 8 the next step's fragment (b0 a0 b1 a1 b2 a2 b3 a3), then - with
-  // loads - direct load i / 2 after every odd MFMA.
+  // One K step in fixed order: MFMA i = (vi, ti) = (i / kNF, i % kNF), then
+  // for i < 2 kNF the next step's fragment (b0 a0 b1 a1 ...), then - with
+  // loads - the stage's kLoads direct loads spread evenly over the MFMAs.
   using XT = std::integral_constant<bool, kXT>;
   using YT = std::integral_constant<bool, kYT>;
-  auto step = [&](const bf16x8 (&a)[4], const bf16x8 (&b)[4], const uint8_t* nst, int nuu,
-                  bf16x8 (&na)[4], bf16x8 (&nb)[4], const LoadCtx& lc, auto op, auto with_loads) {
+  auto step = [&](const bf16x8 (&a)[kNF], const bf16x8 (&b)[kNF], const uint8_t* nst, int nuu,
+                  bf16x8 (&na)[kNF], bf16x8 (&nb)[kNF], const LoadCtx& lc, auto op,
+                  auto with_loads) {
+    constexpr int kStride = kNF * kNF / kLoads;     // MFMAs per load
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int vi = i >> 2, ti = i & 3;
+    for (int i = 0; i < kNF * kNF; ++i) {
+      const int vi = i / kNF, ti = i % kNF;
       acc[vi][ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[vi], b[ti], acc[vi][ti], 0, 0, 0);
-      if (i < 8) {
+      if (i < 2 * kNF) {
         if (i & 1) na[i >> 1] = frag(nst, xoff[i >> 1], nuu, XT{});
         else nb[i >> 1] = frag(nst, yoff[i >> 1], nuu, YT{});
       }
       if constexpr (decltype(with_loads)::value) {
-        if (i & 1) load_one(lc, op, i >> 1);
+        if (i % kStride == kStride - 1) load_one(lc, op, i / kStride);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto read_frags = [&](const uint8_t* st, int uu, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
+  auto read_frags = [&](const uint8_t* st, int uu, bf16x8 (&a)[kNF], bf16x8 (&b)[kNF]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kNF; ++i) {
       b[i] = frag(st, yoff[i], uu, YT{});
       a[i] = frag(st, xoff[i], uu, XT{});
     }
@@ -320,7 +330,7 @@ __device__ __forceinline__ void det_gemm_body(const GemmParams& g) {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
 
-  bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+  bf16x8 fa0[kNF], fb0[kNF], fa1[kNF], fb1[kNF];
   using OpX = std::integral_constant<int, 0>;
   using OpY = std::integral_constant<int, 1>;
 
@@ -357,18 +367,18 @@ __device__ __forceinline__ void det_gemm_body(const GemmParams& g) {
   }
   wait_vmcnt<0>();             // loads past the end must land before LDS is released
 
-  // ---- store: acc[vi][ti][r] = D[p][q] with q = q0 + wt*128 + ti*32 + (lane & 31)
-  // and p = p0 + wv*128 + vi*32 + 8*(r/4) + 4*half + (r%4): four consecutive p
+  // ---- store: acc[vi][ti][r] = D[p][q] with q = q0 + wt*kHalf + ti*32 + (lane & 31)
+  // and p = p0 + wv*kHalf + vi*32 + 8*(r/4) + 4*half + (r%4): four consecutive p
   // per (vi, r / 4), one 16-byte (fp32) or 8-byte (bf16) store.
 #pragma unroll
-  for (int ti = 0; ti < 4; ++ti) {
-    const int64_t q = q0 + wt * 128 + ti * 32 + (lane & 31);
+  for (int ti = 0; ti < kNF; ++ti) {
+    const int64_t q = q0 + wt * kHalf + ti * 32 + (lane & 31);
     if (q >= g.Q) continue;
 #pragma unroll
-    for (int vi = 0; vi < 4; ++vi)
+    for (int vi = 0; vi < kNF; ++vi)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int64_t p = p0 + wv * 128 + vi * 32 + 8 * r4 + 4 * half;
+        const int64_t p = p0 + wv * kHalf + vi * 32 + 8 * r4 + 4 * half;
         if (p >= g.P) continue;
         const floatx4 v = {acc[vi][ti][4 * r4], acc[vi][ti][4 * r4 + 1],
                            acc[vi][ti][4 * r4 + 2], acc[vi][ti][4 * r4 + 3]};
@@ -386,28 +396,42 @@ __device__ __forceinline__ void det_gemm_body(const GemmParams& g) {
 }
 
 __global__ __launch_bounds__(kThreads, 1) void det_gemm_nn_kernel(const GemmParams g) {
-  det_gemm_body<false, false>(g);
+  det_gemm_body<false, false, 256>(g);
 }
 __global__ __launch_bounds__(kThreads, 1) void det_gemm_tn_kernel(const GemmParams g) {
-  det_gemm_body<true, false>(g);
+  det_gemm_body<true, false, 256>(g);
 }
 __global__ __launch_bounds__(kThreads, 1) void det_gemm_tt_kernel(const GemmParams g) {
-  det_gemm_body<true, true>(g);
+  det_gemm_body<true, true, 256>(g);
+}
+__global__ __launch_bounds__(kThreads, 1) void det_gemm_nn_t128_kernel(const GemmParams g) {
+  det_gemm_body<false, false, 128>(g);
+}
+__global__ __launch_bounds__(kThreads, 1) void det_gemm_tn_t128_kernel(const GemmParams g) {
+  det_gemm_body<true, false, 128>(g);
+}
+__global__ __launch_bounds__(kThreads, 1) void det_gemm_tt_t128_kernel(const GemmParams g) {
+  det_gemm_body<true, true, 128>(g);
 }
 
 }  // namespace
 
-hipError_t launch_det_gemm(const GemmParams& g, bool x_t, bool y_t, hipStream_t stream) {
+hipError_t launch_det_gemm(const GemmParams& g_in, bool x_t, bool y_t, hipStream_t stream) {
+  if (!x_t && y_t) return hipErrorInvalidValue;
+  // 128 x 128 tiles when 256 x 256 tiles would leave compute units idle
+  GemmParams g = g_in;
+  const int64_t tiles256 = ((g.P + 255) / 256) * ((g.Q + 255) / 256);
+  const int kt = (g.cu_count > 0 && tiles256 < g.cu_count) ? 128 : 256;
+  g.Pt = (int32_t)((g.P + kt - 1) / kt);
+  g.Qt = (int32_t)((g.Q + kt - 1) / kt);
   const int64_t blocks = (int64_t)g.Pt * g.Qt;
   if (blocks <= 0) return hipSuccess;
-  if (!x_t && !y_t)
-    hipLaunchKernelGGL(det_gemm_nn_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, g);
-  else if (x_t && !y_t)
-    hipLaunchKernelGGL(det_gemm_tn_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, g);
-  else if (x_t && y_t)
-    hipLaunchKernelGGL(det_gemm_tt_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, g);
+  void (*k)(const GemmParams);
+  if (kt == 128)
+    k = !x_t ? det_gemm_nn_t128_kernel : (y_t ? det_gemm_tt_t128_kernel : det_gemm_tn_t128_kernel);
   else
-    return hipErrorInvalidValue;
+    k = !x_t ? det_gemm_nn_kernel : (y_t ? det_gemm_tt_kernel : det_gemm_tn_kernel);
+  hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(kThreads), 0, stream, g);
   return hipGetLastError();
 }
 

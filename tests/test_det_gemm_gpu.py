@@ -159,3 +159,21 @@ def test_det_linear_autograd():
     y32.backward(g.float())
     torch.cuda.synchronize()
     assert torch.equal(a2.grad, ila.det_gemm_da(g, w.detach()))
+
+
+def test_tile_sizes_give_the_same_bits():
+    """A full batch with 256 x 256 tiles for every compute unit and row chunks
+    small enough for 128 x 128 tiles: the same rows, bit for bit (forward and
+    dA; every output is one MFMA chain whatever the tile)."""
+    M, N, K = 4096, 4096, 256
+    a, b = bf16((M, K), 17), bf16((N, K), 18)
+    dc, b2 = bf16((M, 256), 19), bf16((256, 4096), 20)
+    say("det_gemm 256- vs 128-tiles")
+    full_c = ila.det_gemm(a, b, out_dtype=torch.float32)            # 16 x 16 tiles of 256
+    full_da = ila.det_gemm_da(dc, b2, out_dtype=torch.float32)      # 16 x 16 tiles of 256
+    parts_c = [ila.det_gemm(a[i:i + 300], b, out_dtype=torch.float32) for i in range(0, M, 300)]
+    parts_da = [ila.det_gemm_da(dc[i:i + 300], b2, out_dtype=torch.float32)
+                for i in range(0, M, 300)]
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(parts_c), full_c)
+    assert torch.equal(torch.cat(parts_da), full_da)
