@@ -40,7 +40,7 @@ PEAK_HBM_GBPS = 8000.0
 # the kernel source the counters were taken on (comments and whitespace stripped): any
 # change to the code reports null.
 MEASURED_TRAFFIC = {
-    ("headline", "260dcd430782985c"): {"fetch_bytes": 6628049767, "write_bytes": 3094896},  # same machine code as 3aebc68a726ebe98, where the counters were taken
+    ("headline", "260dcd430782985c"): {"fetch_bytes": 6619756034, "write_bytes": 3093080},
 }
 
 
@@ -140,22 +140,28 @@ def invariance_cost(h, t, w, b, steps=10, warmup=3):
 
 
 def det_gemm_leg(steps=10, warmup=3):
-    """The deterministic GEMM (forward, dA, dB) at M = N = K = 4096 and at the
-    largest shape of the page's own table (M, K, N = 512, 1024, 1024), with
-    torch's bf16 matmul (hipBLASLt, not deterministic by contract) beside it."""
+    """The deterministic GEMM (forward, dA, dB, and forward + dA + dB) at M = N = K
+    = 4096 and at the three shapes of the page's own table (M x K x N = 128 x 128
+    x 128, 256 x 512 x 512, 512 x 1024 x 1024), with torch's bf16 matmul
+    (hipBLASLt, not deterministic by contract) beside them."""
     import torch
     import invariant_linear_log_amd as ila
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev).manual_seed(11)
     out = {"peak_tflops": PEAK_BF16_TFLOPS}
-    for (M, N, K) in ((4096, 4096, 4096), (512, 1024, 1024)):
+    for (M, N, K) in ((4096, 4096, 4096), (128, 128, 128), (256, 512, 512), (512, 1024, 1024)):
         a = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
         b = torch.randn((N, K), generator=g, device=dev).to(torch.bfloat16)
         dc = torch.randn((M, N), generator=g, device=dev).to(torch.bfloat16)
         bt = b.t().contiguous()              # [K, N] once, outside the timed calls
         flops = 2.0 * M * N * K
+
+        def fwd_bwd():
+            ila.det_gemm(a, b)
+            ila.det_gemm_da(dc, b)
+            ila.det_gemm_db(a, dc)
         runs = {"fwd": lambda: ila.det_gemm(a, b), "da": lambda: ila.det_gemm_da(dc, b),
-                "db": lambda: ila.det_gemm_db(a, dc),
+                "db": lambda: ila.det_gemm_db(a, dc), "fwd_bwd": fwd_bwd,
                 "torch_matmul_fwd": lambda: torch.matmul(a, bt)}
         rec = {}
         for name, fn in runs.items():
@@ -169,7 +175,8 @@ def det_gemm_leg(steps=10, warmup=3):
             e1.record()
             e1.synchronize()
             ms = e0.elapsed_time(e1) / steps
-            rec[name] = {"ms": ms, "tflops": flops / ms / 1e9}
+            f = 3 * flops if name == "fwd_bwd" else flops
+            rec[name] = {"ms": ms, "tflops": f / ms / 1e9}
         rec["fwd"]["frac"] = rec["fwd"]["tflops"] / PEAK_BF16_TFLOPS
         out[f"M{M}_N{N}_K{K}"] = rec
     return out
