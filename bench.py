@@ -36,11 +36,11 @@ PEAK_HBM_GBPS = 8000.0
 
 # HBM-side bytes per launch of proj_lse_kernel on the headline workload, from two
 # rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE), each scaled by what the same counter
-# reads for a plain 1 GiB device copy (x2.000 and x1.000).  Keyed by code_digest() of
-# the kernel source the counters were taken on (comments and whitespace stripped): any
-# change to the code reports null.
+# reads for a plain 1 GiB device copy (x2.000 and x1.000).  Keyed by projection_digest()
+# of the code the counters were taken on (the kernel and its launch code, comments and
+# whitespace stripped): any change to that code reports null.
 MEASURED_TRAFFIC = {
-    ("headline", "260dcd430782985c"): {"fetch_bytes": 6619756034, "write_bytes": 3093080},
+    ("headline", "bf39184e5398cf03"): {"fetch_bytes": 6351834407, "write_bytes": 18810216},
 }
 
 
@@ -85,22 +85,32 @@ def algorithmic_bytes(N, H, V, S, bias_bytes):
     return (V * H * 2 + N * H * 2 + N * 8 + bias_bytes + 2 * N * S * 8 + 2 * N * 4 + 2 * N * 4)
 
 
-def code_digest(path):
-    """sha256 prefix of a C++/HIP source with comments and whitespace removed:
-    edits to comments alone keep it, any change to the code changes it."""
+def code_digest(*paths):
+    """sha256 prefix of C++/HIP sources with comments and whitespace removed
+    (concatenated in the order given): edits to comments alone keep it, any
+    change to the code changes it."""
     import hashlib
     import re
-    with open(path) as f:
-        text = f.read()
+    text = ""
+    for path in paths:
+        with open(path) as f:
+            text += f.read()
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
     text = re.sub(r"\s+", "", text)
     return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
+def projection_digest():
+    """code_digest of what decides the projection kernel's memory traffic: the
+    kernel source and the host code that picks its launch (row blocks, split
+    runs)."""
+    csrc = os.path.join(ROOT, "invariant_linear_log_amd", "csrc")
+    return code_digest(os.path.join(csrc, "proj_lse.hip"), os.path.join(csrc, "bilogp_host.cpp"))
+
+
 def measured_traffic(workload):
-    src = os.path.join(ROOT, "invariant_linear_log_amd", "csrc", "proj_lse.hip")
-    rec = MEASURED_TRAFFIC.get((workload, code_digest(src)))
+    rec = MEASURED_TRAFFIC.get((workload, projection_digest()))
     return None if rec is None else rec["fetch_bytes"] + rec["write_bytes"]
 
 

@@ -14,7 +14,8 @@
  * contiguous splits whose count depends on V only (the page's annotation on
  * select_batch_invariant_vocab_splits).  Each split yields a per-row partial
  * online-softmax state (running max, rescaled sum of exponentials); the
- * partials are combined in ascending split order ("What this PR changes").
+ * partials are combined in ascending split order ("What this PR changes"),
+ * as one pairwise tree over ascending split index, the same for every N.
  * The bits of row i's outputs depend only on row i's inputs, W, bias, H and
  * V: never on N, on the position of the row in the batch, on the other rows,
  * or on the number of compute units.
@@ -215,9 +216,10 @@ bilogp_status bilogp_partials_range(const void* hidden, const void* weight_slice
                                     int split_end, void* workspace, size_t workspace_bytes,
                                     void* stream);
 
-/* bilogp_merge: the ascending combine of the partials left in `workspace` by
- * bilogp_partials for the same N, V and target (PR #337, description:
- * "ascending combine"); writes logp_out and lse_out, fp32 [N]. */
+/* bilogp_merge: the combine, in ascending split order, of the partials left
+ * in `workspace` by bilogp_partials (or by bilogp_partials_range over every
+ * split) for the same N, V and target (PR #337, description, "What this PR
+ * changes"); writes logp_out and lse_out, fp32 [N]. */
 bilogp_status bilogp_merge(const int64_t* target, const void* workspace, size_t workspace_bytes,
                            float* logp_out, float* lse_out, int64_t N, int64_t V, void* stream);
 

@@ -9,7 +9,7 @@ namespace bilogp {
 // Part of the bit contract: the vocabulary tile width and the largest split
 // count decide which columns are reduced together and in which order.
 constexpr int kVtileCols = 256;
-constexpr int kMaxSplits = 64;
+constexpr int kMaxSplits = 256;
 
 // Cap of the throughput split policy (not part of the invariant contract).
 constexpr int kMaxThroughputSplits = 1024;
@@ -36,12 +36,16 @@ struct ProjParams {
   int32_t S;               // splits
   int32_t rows;            // tokens per row block: 256, or 128 for small batches
   int32_t R;               // row blocks, ceil(N / rows)
-  // the launch covers splits [split0, split0 + S_grid) of the S.  weight and
+  // the launch covers splits [split0, split1) of the S, in runs of spg
+  // consecutive splits per workgroup (S_grid = ceil((split1 - split0) / spg)
+  // runs; the last may be shorter).  weight and
   // bias are addressed by absolute vocabulary column: for a launch whose
   // weight holds columns from col0 on, the host passes the weight address
   // minus col0 rows (and the bias copy's address minus col0 entries); every
   // address the kernel forms stays inside the slice
   int32_t split0;
+  int32_t split1;
+  int32_t spg;
   int32_t S_grid;
   int64_t col0;
   // backward only (softmax-gradient kernel): the forward's lse, the upstream

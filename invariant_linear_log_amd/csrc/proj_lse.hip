@@ -7,8 +7,11 @@
 // per-row online-softmax partial (running max m, sum s of exp(z - m)).  The
 // partials are merged by merge.hip.
 //
-// Workgroup: 512 threads (8 wave64s), one (row block of 256 tokens, split)
-// (or 128 tokens, below).
+// Workgroup: 512 threads (8 wave64s), one row block of 256 tokens (or 128,
+// below) and a run of consecutive splits: their tiles are one contiguous
+// range, computed back to back, and a partial is written (and the running
+// state restarted) where each split ends.  How many splits a workgroup takes
+// only schedules the work: every split's partial is the same either way.
 // Per vocabulary tile of 256 columns the workgroup computes the 256 x 256
 // product W_tile[256, H] . hidden_block[256, H]^T with
 // v_mfma_f32_32x32x16_bf16, W as the A operand (MFMA rows = vocabulary) and
@@ -162,11 +165,12 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
   const int wt = wave >> 1;
   const int half = lane >> 5;
 
-  // Block id -> (split, row block); a bijection that only orders the work.
-  // Blocks go to the eight XCDs round-robin: first give each XCD a contiguous
-  // run of tile indices, then order tiles in groups of kRowBlockGroup row
-  // blocks x all splits (row blocks fastest), so the ~32 tiles an XCD runs at
-  // once share a few W slices and a few hidden blocks in its L2.
+  // Block id -> (split run, row block); a bijection that only orders the
+  // work.  Blocks go to the eight XCDs round-robin: first give each XCD a
+  // contiguous run of tile indices, then order tiles in groups of
+  // kRowBlockGroup row blocks x all split runs (row blocks fastest), so the
+  // ~32 tiles an XCD runs at once share a few W slices and a few hidden
+  // blocks in its L2.
   const int nblk = p.R * p.S_grid;
   const int per_xcd = nblk >> 3;
   int u = blockIdx.x;
@@ -175,12 +179,13 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
   const int first_rb = (u / in_group) * kRowBlockGroup;
   const int group_rbs = min(p.R - first_rb, kRowBlockGroup);
   const int rb = first_rb + (u % in_group) % group_rbs;
-  const int split = p.split0 + (u % in_group) / group_rbs;
+  const int split_first = p.split0 + (u % in_group) / group_rbs * p.spg;
+  const int split_last = min(split_first + p.spg, p.split1);     // exclusive
 
   const int64_t m0 = (int64_t)rb * kRows;
   const int rows_here = (int)min((int64_t)kRows, p.N - m0);
-  const int vt_begin = split * p.vps;
-  const int nvt = min(vt_begin + p.vps, p.T) - vt_begin;
+  const int vt_begin = split_first * p.vps;
+  const int nvt = min(split_last * p.vps, p.T) - vt_begin;
   const int H = p.H;
   // K stages per tile, padded to an even count with stages that read only
   // zeros (they leave the accumulators unchanged), so every tile starts in
@@ -411,6 +416,45 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
     s_run[ti] = 0.f;
   }
 
+  // A split ends (its last tile is folded into m_run / s_run): merge the
+  // lane halves, then the two vocabulary-half waves (through LDS), write the
+  // split's partial and restart the running state.  The barrier waits for
+  // LDS only: the next stages' loads stay in flight.  `red` is free again by
+  // the next flush, at least one stage barrier later.
+  auto flush = [&](int split) {
+    float mm[kTi], ss[kTi];
+#pragma unroll
+    for (int ti = 0; ti < kTi; ++ti) {
+      const float om = __shfl_xor(m_run[ti], 32);
+      const float os = __shfl_xor(s_run[ti], 32);
+      if (half == 0)
+        merge_state(m_run[ti], s_run[ti], om, os, mm[ti], ss[ti]);
+      else
+        merge_state(om, os, m_run[ti], s_run[ti], mm[ti], ss[ti]);
+    }
+    if (wv == 1 && half == 0) {
+#pragma unroll
+      for (int ti = 0; ti < kTi; ++ti)
+        red[wt * kWaveTok + ti * 32 + lane] = make_float2(mm[ti], ss[ti]);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (wv == 0 && half == 0) {
+#pragma unroll
+      for (int ti = 0; ti < kTi; ++ti) {
+        const int j = wt * kWaveTok + ti * 32 + lane;
+        const float2 hi = red[j];
+        float m, s;
+        merge_state(mm[ti], ss[ti], hi.x, hi.y, m, s);
+        if (j < rows_here) p.part[(m0 + j) * p.S + split] = make_float2(m, s);
+      }
+    }
+#pragma unroll
+    for (int ti = 0; ti < kTi; ++ti) {
+      m_run[ti] = -INFINITY;
+      s_run[ti] = 0.f;
+    }
+  };
+
   // Prologue: stage 0 whole and the W slice of stage 1 (its hidden slice is
   // issued in stage 0).
   {
@@ -552,41 +596,15 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
       m_run[ti] = m_new;
     }
     __builtin_amdgcn_sched_barrier(0);      // the tile is consumed before the next one starts
+    const int vt = vt_begin + v;
+    if (v + 1 == nvt || (vt + 1) % p.vps == 0) flush(vt / p.vps);
+    __builtin_amdgcn_sched_barrier(0);
     init_acc(v + 1);
   }
 
   // The last stages issued loads past the end (into buffers nobody reads);
   // let them land before the workgroup's LDS is released.
   wait_vmcnt<0>();
-
-  if constexpr (kGrad) return;
-
-  // ---- split done: merge lane halves, then the two vocabulary-half waves ----
-  float mm[kTi], ss[kTi];
-#pragma unroll
-  for (int ti = 0; ti < kTi; ++ti) {
-    const float om = __shfl_xor(m_run[ti], 32);
-    const float os = __shfl_xor(s_run[ti], 32);
-    if (half == 0)
-      merge_state(m_run[ti], s_run[ti], om, os, mm[ti], ss[ti]);
-    else
-      merge_state(om, os, m_run[ti], s_run[ti], mm[ti], ss[ti]);
-  }
-  if (wv == 1 && half == 0) {
-#pragma unroll
-    for (int ti = 0; ti < kTi; ++ti) red[wt * kWaveTok + ti * 32 + lane] = make_float2(mm[ti], ss[ti]);
-  }
-  __syncthreads();
-  if (wv == 0 && half == 0) {
-#pragma unroll
-    for (int ti = 0; ti < kTi; ++ti) {
-      const int j = wt * kWaveTok + ti * 32 + lane;
-      const float2 hi = red[j];
-      float m, s;
-      merge_state(mm[ti], ss[ti], hi.x, hi.y, m, s);
-      if (j < rows_here) p.part[(m0 + j) * p.S + split] = make_float2(m, s);
-    }
-  }
 }
 
 __global__ __launch_bounds__(kThreads, 1) void proj_lse_kernel(const ProjParams p) {

@@ -197,7 +197,7 @@ def vocab_splits_throughput(N: int, V: int, cu_count: int, vtile: int = 256,
 
 
 def split_merge_linear_logp(hidden, weight, target, bias=None, vtile: int = 256,
-                            max_splits: int = 64,
+                            max_splits: int = 256,
                             rows: Optional[Sequence[int]] = None,
                             splits: Optional[Sequence[Tuple[int, int]]] = None
                             ) -> Tuple[np.ndarray, np.ndarray]:

@@ -254,7 +254,7 @@ def pin_split_policy(orc):
     tiles, at most max_splits of them; plus worked values of the formula."""
     for V in list(range(1, 3000, 7)) + [16383, 16384, 16385, 32000, 65536, 128256, 151936,
                                          152064, 256 * 64 * 3 + 1, 10 ** 6, 2 ** 31 - 1]:
-        for vt, mx in ((256, 64), (128, 8), (64, 1)):
+        for vt, mx in ((256, 256), (256, 64), (128, 8), (64, 1)):
             r = orc.vocab_splits(V, vt, mx)
             tiles = -(-V // vt)
             _assert(r[0][0] == 0 and r[-1][1] == tiles, f"cover V={V}")
@@ -264,7 +264,19 @@ def pin_split_policy(orc):
             sizes = [b - a for a, b in r]
             _assert(all(s == sizes[0] for s in sizes[:-1]) and sizes[-1] <= sizes[0],
                     f"uneven split V={V}")
-    # worked: V=128256 -> 501 tiles of 256, 8 per split, 63 splits (last has 5)
+    # worked, at most 256 splits: V=128256 -> 501 tiles of 256, 2 per split,
+    # 251 splits (the last has one tile)
+    r = orc.vocab_splits(128256, 256, 256)
+    _assert(len(r) == 251 and r[0] == (0, 2) and r[-1] == (500, 501), "V=128256 splits, 256")
+    r = orc.vocab_splits(152064, 256, 256)     # 594 tiles -> 3 per split -> 198 splits
+    _assert(len(r) == 198 and r[1] == (3, 6) and r[-1] == (591, 594), "V=152064 splits, 256")
+    r = orc.vocab_splits(256 * 256, 256, 256)  # 256 tiles -> 256 splits of one tile
+    _assert(len(r) == 256 and r[-1] == (255, 256), "V=65536 splits, 256")
+    r = orc.vocab_splits(256 * 256 + 1, 256, 256)  # 257 tiles -> 2 per split -> 129
+    _assert(len(r) == 129 and r[-1] == (256, 257), "V=65537 splits, 256")
+    r = orc.vocab_splits(32000, 256, 256)      # 125 tiles -> 125 splits of one tile
+    _assert(len(r) == 125 and r[-1] == (124, 125), "V=32000 splits, 256")
+    # worked, at most 64 splits: V=128256 -> 8 per split, 63 splits (last has 5)
     r = orc.vocab_splits(128256, 256, 64)
     _assert(len(r) == 63 and r[0] == (0, 8) and r[-1] == (496, 501), "V=128256 splits")
     r = orc.vocab_splits(151936, 256, 64)      # 594 tiles -> 10 per split -> 60 splits
@@ -319,7 +331,7 @@ def pin_split_merge_equals_plain(orc):
     definition (they are equal in real arithmetic) across tails and split counts."""
     cases = [(4, 16, 1000, 256, 64), (3, 32, 2000, 256, 64), (5, 16, 1031, 64, 4),
              (2, 24, 16641, 256, 64), (3, 8, 1, 256, 64), (2, 8, 257, 256, 64),
-             (3, 16, 5000, 128, 3)]
+             (3, 16, 5000, 128, 3), (3, 16, 70001, 256, 256)]
     for j, (N, H, V, vt, mx) in enumerate(cases):
         inp = synth.make_custom(N, H, V, seed=50 + j, bias="f32" if j % 2 else None)
         lp1, ls1 = orc.linear_logp(inp["hidden"], inp["weight"], inp["target"], inp["bias"])

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 def test_constants_and_version():
     assert ila.bilogp_abi_version() == 1
     assert ila.bilogp_vtile_cols() == 256
-    assert ila.bilogp_max_splits() == 64
+    assert ila.bilogp_max_splits() == 256
     for s in range(5):
         assert ila.bilogp_status_string(s) != "unknown status"
     assert ila.bilogp_status_string(99) == "unknown status"
@@ -45,7 +45,8 @@ def test_constants_and_version():
 
 def _policy_values():
     vs = list(range(1, 5000, 13)) + [16383, 16384, 16385, 32000, 65536, 128256, 151936, 152064,
-                                      256 * 64 * 7 + 1, 10 ** 6, 2 ** 30]
+                                      256 * 64 * 7 + 1, 256 * 256, 256 * 256 + 1, 256 * 512 + 1,
+                                      10 ** 6, 2 ** 30]
     return vs
 
 
@@ -179,12 +180,13 @@ def test_forward_mode_fails_closed(mode, cu, status):
 
 
 def test_forward_mode_workspace_is_per_mode():
-    # enough for the invariant mode's 63 splits of V=128256, but the throughput
-    # mode at N=8 takes 251: the size check uses the mode's own split count
+    # enough for the invariant mode's 251 splits of V=128256, but the throughput
+    # mode at N=8 with 1024 compute units takes 501: the size check uses the
+    # mode's own split count
     lib = ila.load_library()
     need_inv = ila.bilogp_workspace_bytes(8, 128256)
     st = lib.bilogp_forward_mode(FAKE, FAKE + 0x10000000, FAKE + 0x200000, None, 0, FAKE + 0x300000,
-                                 FAKE + 0x400000, 8, 64, 128256, B.BILOGP_SPLITS_THROUGHPUT, 256,
+                                 FAKE + 0x400000, 8, 64, 128256, B.BILOGP_SPLITS_THROUGHPUT, 1024,
                                  FAKE + 0x40000000, need_inv, None)
     assert st == B.BILOGP_E_WORKSPACE, (st, ila.bilogp_last_error())
 
@@ -408,18 +410,19 @@ def _call_range(begin, end, N=8, V=128256, H=64, bias=None, bias_dtype=0):
                                      H, V, begin, end, FAKE + 0x40000000, 1 << 24, None)
 
 
-@pytest.mark.parametrize("begin,end", [(-1, 3), (3, 3), (5, 2), (0, 64), (62, 64), (0, -1)])
+@pytest.mark.parametrize("begin,end", [(-1, 3), (3, 3), (5, 2), (0, 252), (250, 252), (0, -1)])
 def test_partials_range_rejects_bad_ranges(begin, end):
-    # V = 128256 has 63 splits
+    # V = 128256 has 251 splits
     assert _call_range(begin, end) == B.BILOGP_E_INVALID_ARG, ila.bilogp_last_error()
     assert _call_range(begin, end, N=0) == B.BILOGP_E_INVALID_ARG
 
 
 def test_partials_range_empty_batch_and_columns():
-    assert _call_range(0, 63, N=0) == B.BILOGP_OK
+    assert _call_range(0, 251, N=0) == B.BILOGP_OK
     assert _call_range(10, 20, N=0) == B.BILOGP_OK
-    assert ila.vocab_split_columns(128256, 0, 63) == (0, 128256)
-    assert ila.vocab_split_columns(128256, 7, 9) == (7 * 8 * 256, 9 * 8 * 256)
+    assert ila.vocab_split_columns(128256, 0, 251) == (0, 128256)
+    assert ila.vocab_split_columns(128256, 7, 9) == (7 * 2 * 256, 9 * 2 * 256)
+    assert ila.vocab_split_columns(128256, 250, 251) == (500 * 256, 128256)
     assert ila.vocab_split_columns(1000, 3, 4) == (768, 1000)
 
 

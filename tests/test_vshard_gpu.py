@@ -24,9 +24,9 @@ def _ranges(S, cuts):
 
 CASES = [  # N, H, V, bias, seed, cut points (split indices)
     (300, 520, 5003, None, 1, [3, 11]),          # 20 splits of one tile, vocabulary tail
-    (257, 264, 70000, "bf16", 2, [1, 27, 54]),   # 55 splits of 5 tiles, last split 4 tiles
-    (1, 4096, 16385, "f32", 3, [16, 32]),        # 33 splits, last split one column
-    (4096, 4096, 128256, None, 4, [8, 16, 24, 32, 40, 48, 56]),   # 8-way share of the headline
+    (257, 264, 70000, "bf16", 2, [1, 27, 54, 100]),   # 137 splits of 2 tiles, last tile partial
+    (1, 4096, 16385, "f32", 3, [16, 32]),        # 65 splits, last split one column
+    (4096, 4096, 128256, None, 4, [32, 64, 96, 128, 160, 192, 224]),   # 8-way share of the headline
 ]
 
 
