@@ -4,7 +4,7 @@ one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline]
                     [--no-cpu-baseline] [--no-backward] [--no-det-gemm]
-                    [--no-invariance-cost] [--no-shard-share]
+                    [--no-invariance-cost] [--no-shard-share] [--no-library-context]
 
 One step is one full pass of the hot path over one batch: bilogp_partials
 (fused bf16-MFMA projection + per-split online softmax) followed by
@@ -55,6 +55,9 @@ def parse():
                     help="skip timing the deterministic GEMM (forward, dA, dB)")
     ap.add_argument("--no-shard-share", action="store_true",
                     help="skip timing one GPU's share of an 8-way vocabulary or row sharding")
+    ap.add_argument("--no-library-context", action="store_true",
+                    help="skip timing torch's matmul (hipBLASLt) and the unfused matmul + "
+                         "logsumexp path at the workload's shape")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip timing the deterministic backward")
     ap.add_argument("--no-invariance-cost", action="store_true",
@@ -276,6 +279,44 @@ def shard_share_leg(h, t, w, b, ranks=8, steps=10, warmup=3):
                           "frac": fn_ / ns_ms / 1e9 / PEAK_BF16_TFLOPS}}
 
 
+def library_context_leg(h, t, w, b, steps=10, warmup=3):
+    """Context, not the product: the same contraction through torch's bf16 matmul
+    (hipBLASLt; z = hidden . W^T materialised as bf16 [N, V], no softmax), and the
+    unfused path a caller would otherwise run (that matmul, the bias added in
+    float32, a float32 logsumexp over V and a gather of the target logit).  Neither is batch-
+    invariant by contract."""
+    import torch
+    h2 = h.reshape(-1, h.shape[-1])
+    t2 = t.reshape(-1)
+    N, H = h2.shape
+    V = w.shape[0]
+
+    def gemm():
+        return torch.matmul(h2, w.t())
+
+    def unfused():
+        z = torch.matmul(h2, w.t()).float()
+        if b is not None:
+            z = z + b.float()
+        lse = torch.logsumexp(z, dim=-1)
+        return z.gather(1, t2[:, None])[:, 0] - lse, lse
+    rec = {}
+    for name, fn in (("hipblaslt_gemm", gemm), ("unfused_matmul_logsumexp", unfused)):
+        for _ in range(warmup):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        rec[name] = {"ms": ms, "tflops": 2.0 * N * H * V / ms / 1e9}
+    torch.cuda.empty_cache()
+    return rec
+
+
 def device_info(dev):
     import torch
     prop = torch.cuda.get_device_properties(dev)
@@ -437,6 +478,8 @@ def main():
         out["shard_share"] = shard_share_leg(h, t, w, b)
     if not args.no_det_gemm:
         out["det_gemm"] = det_gemm_leg()
+    if not args.no_library_context:
+        out["library_context"] = library_context_leg(h, t, w, b)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows)
     print(json.dumps(out), flush=True)
