@@ -137,9 +137,10 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 // The kernel body, instantiated with and without bias, and (kGrad) as the
 // softmax-gradient pass of the backward: the same tiles and the same
 // accumulation, with an epilogue that writes dZ instead of reducing it.
-template <bool kHasBias, bool kGrad, int kTi>
+template <bool kHasBias, bool kGrad, int kTi, int kSlots = 2>
 __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
   static_assert(kTi == 1 || kTi == 2, "one or two 32-token columns per wave");
+  static_assert(kSlots == 2 || (kSlots == 3 && kTi == 1), "three buffers fit 128-token blocks");
   constexpr int kRows = 128 * kTi;                 // tokens per row block
   constexpr int kWaveTok = 32 * kTi;               // tokens per wave
   constexpr int kLoadsH = kRows * kLdsRowBytes / (kThreads * 16);   // hidden loads per stage
@@ -147,15 +148,20 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
   // of one from a direct-to-LDS load into the other and does not drain the
   // load pipeline before every read.  Buffer layout: W slice (32 KB), hidden
   // slice (32 KB).
-  __shared__ __attribute__((aligned(1024))) uint8_t slot0[kSlotBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t slot1[kSlotBytes];
+  // With three buffers (128-token blocks only) each holds the 32 KB W slice
+  // and the 16 KB hidden slice: 144 KB in all.
+  constexpr int kBuf = kSlots == 2 ? kSlotBytes : kTileBytes + kRows * kLdsRowBytes;
+  __shared__ __attribute__((aligned(1024))) uint8_t slot0[kBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot1[kBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot2[kSlots == 3 ? kBuf : 16];
   __shared__ float2 red[kBlockRows];
   // bias of the current and the next vocabulary tile (bias kernels only)
   __shared__ __attribute__((aligned(16))) float bias_lds[2][kVtileCols];
 
   auto slot_ptr = [&](auto sc) -> uint8_t* {
     if constexpr (decltype(sc)::value == 0) return slot0;
-    else return slot1;
+    else if constexpr (decltype(sc)::value == 1) return slot1;
+    else return slot2;
   };
 
   const int tid = threadIdx.x;
@@ -187,10 +193,10 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
   const int vt_begin = split_first * p.vps;
   const int nvt = min(split_last * p.vps, p.T) - vt_begin;
   const int H = p.H;
-  // K stages per tile, padded to an even count with stages that read only
-  // zeros (they leave the accumulators unchanged), so every tile starts in
-  // buffer 0 and ends in buffer 1.
-  const int KT = ((H + kBK - 1) / kBK + 1) / 2 * 2;
+  // K stages per tile, padded to a multiple of the buffer count with stages
+  // that read only zeros (they leave the accumulators unchanged), so every
+  // tile starts in buffer 0 and ends in the last buffer.
+  const int KT = ((H + kBK - 1) / kBK + kSlots - 1) / kSlots * kSlots;
   const int G = nvt * KT;                          // stages in this workgroup
 
   // ---- per-lane load descriptors: 4 + kLoadsH direct-to-LDS loads per stage --
@@ -393,6 +399,13 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
     wait_vmcnt<0>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
+  // Three buffers: the loads still allowed in flight are the W slice of the
+  // stage after next and the hidden slice of the next stage (issued after
+  // everything the next stage needs; the load counter completes in order).
+  auto sync_stage3 = [&]() {
+    wait_vmcnt<kLoadsPerOperand + kLoadsH>();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
 
   bf16x8 fa0[4], fb0[kTi], fa1[4], fb1[kTi];
 
@@ -406,6 +419,20 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
     step(fa0, fb0, st, 3, fa1, fb1, lh, std::false_type{}, std::true_type{});
     sync_stage();
     const LoadCtx lw = ctx_w(g + 2, sc);
+    step(fa1, fb1, slot_ptr(sn), 0, fa0, fb0, lw, std::true_type{}, std::false_type{});
+  };
+  // Stage g with three buffers: SC holds stage g, SN stage g + 1 and SP (free
+  // since the previous stage's barrier) receives the hidden slice of stage
+  // g + 2 under step 0; after this stage's barrier SC receives the W slice of
+  // stage g + 3.  W is requested three stages ahead, hidden two.
+  auto stage3 = [&](int g, auto sc, auto sn, auto sp) {
+    const uint8_t* st = slot_ptr(sc);
+    const LoadCtx lh = ctx_h(g + 2, sp);
+    step(fa0, fb0, st, 1, fa1, fb1, lh, std::true_type{}, std::true_type{});
+    step(fa1, fb1, st, 2, fa0, fb0, lh, std::false_type{}, std::true_type{});
+    step(fa0, fb0, st, 3, fa1, fb1, lh, std::false_type{}, std::true_type{});
+    sync_stage3();
+    const LoadCtx lw = ctx_w(g + 3, sc);
     step(fa1, fb1, slot_ptr(sn), 0, fa0, fb0, lw, std::true_type{}, std::false_type{});
   };
 
@@ -456,7 +483,8 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
   };
 
   // Prologue: stage 0 whole and the W slice of stage 1 (its hidden slice is
-  // issued in stage 0).
+  // issued in stage 0); with three buffers also the hidden slice of stage 1
+  // and the W slice of stage 2.
   {
     const LoadCtx w0 = ctx_w(0, Slot<0>{}), h0 = ctx_h(0, Slot<0>{}), w1 = ctx_w(1, Slot<1>{});
 #pragma unroll
@@ -465,6 +493,13 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
     for (int j = 0; j < kLoadsH; ++j) load_one(h0, j, std::true_type{});
 #pragma unroll
     for (int j = 0; j < kLoadsPerOperand; ++j) load_one(w1, j, std::false_type{});
+    if constexpr (kSlots == 3) {
+      const LoadCtx h1 = ctx_h(1, Slot<1>{}), w2 = ctx_w(2, Slot<2>{});
+#pragma unroll
+      for (int j = 0; j < kLoadsH; ++j) load_one(h1, j, std::true_type{});
+#pragma unroll
+      for (int j = 0; j < kLoadsPerOperand; ++j) load_one(w2, j, std::false_type{});
+    }
     load_bias(0);
   }
   wait_vmcnt<0>();
@@ -472,13 +507,19 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
   init_acc(0);
   read_frags(slot0, 0, fa0, fb0);
 
-  // G is even: stage g lives in buffer 0, stage g + 1 in buffer 1.
-  for (int g = 0; g < G; g += 2) {
-    stage(g, Slot<0>{}, Slot<1>{});
-    stage(g + 1, Slot<1>{}, Slot<0>{});
+  // G is a multiple of kSlots: stage g lives in buffer g % kSlots.
+  for (int g = 0; g < G; g += kSlots) {
+    if constexpr (kSlots == 2) {
+      stage(g, Slot<0>{}, Slot<1>{});
+      stage(g + 1, Slot<1>{}, Slot<0>{});
+    } else {
+      stage3(g, Slot<0>{}, Slot<1>{}, Slot<2>{});
+      stage3(g + 1, Slot<1>{}, Slot<2>{}, Slot<0>{});
+      stage3(g + 2, Slot<2>{}, Slot<0>{}, Slot<1>{});
+    }
 
     const int v = g / KT;
-    if (g + 2 != (v + 1) * KT) continue;
+    if (g + kSlots != (v + 1) * KT) continue;
 
     // ---- epilogue of vocabulary tile v -------------------------------------
     // acc[vi][ti][r] holds z for token column wt*kWaveTok + ti*32 + (lane & 31) and
@@ -622,10 +663,10 @@ __global__ __launch_bounds__(kThreads, 1) void softmax_grad_bias_kernel(const Pr
 // 128-token row blocks: twice the workgroups for batches that 256-token
 // blocks cannot spread over every compute unit; the same bits
 __global__ __launch_bounds__(kThreads, 1) void proj_lse_r128_kernel(const ProjParams p) {
-  proj_lse_body<false, false, 1>(p);
+  proj_lse_body<false, false, 1, 3>(p);
 }
 __global__ __launch_bounds__(kThreads, 1) void proj_lse_bias_r128_kernel(const ProjParams p) {
-  proj_lse_body<true, false, 1>(p);
+  proj_lse_body<true, false, 1, 3>(p);
 }
 __global__ __launch_bounds__(kThreads, 1) void softmax_grad_r128_kernel(const ProjParams p) {
   proj_lse_body<false, true, 1>(p);
