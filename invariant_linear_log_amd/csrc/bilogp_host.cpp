@@ -98,25 +98,34 @@ int32_t row_block_rows(int64_t N, int64_t splits, int dev) {
   return (cu > 0 && r256 * splits < cu) ? 128 : 256;
 }
 
-// Consecutive splits per projection workgroup: runs of about kTilesPerRun
-// vocabulary tiles, fewer where R row blocks x the runs would not cover the
-// device's compute units once, at least one split.  It only schedules the
-// work: each split's partial is written by the same arithmetic however the
-// splits are grouped.  (Measured on MI355X at H = 4096, V = 128256: runs of
-// 4 tiles beat runs of 2, 8, 16 or 32 from N = 256 up, or tie within 1%;
-// runs that leave compute units idle, or split counts that do not divide
-// evenly, cost up to 50%.)
+// Consecutive splits per projection workgroup.  It only schedules the work:
+// each split's partial is written by the same arithmetic however the splits
+// are grouped.  Candidates are 1 .. about kTilesPerRun tiles' worth of
+// splits; the host takes the one whose grid, run in whole rounds of one
+// workgroup per compute unit, ends first: ceil(R * runs / CUs) rounds of that
+// many splits each (a grid that leaves units idle scores its idle share too);
+// ties go to the longer run (fewer workgroup starts).  (Measured on MI355X at H = 4096, V = 128256: runs of 4 tiles beat
+// runs of 2, 8, 16 or 32 from N = 256 up, or tie within 1%, where the rounds
+// come out even; with 3 row blocks, runs of 2 splits left half of the second
+// round idle and took 0.785 ms where runs of 1 split need 3 full rounds.)
 constexpr int kTilesPerRun = 4;
 
 int32_t splits_per_run(int64_t R, int nsplits, int vps, int dev) {
   if (nsplits <= 1) return 1;
-  int32_t spg = std::max(1, kTilesPerRun / std::max(vps, 1));
+  const int32_t cap = std::min(std::max(1, kTilesPerRun / std::max(vps, 1)), nsplits);
   const int cu = g_cu_count[dev].load(std::memory_order_acquire);
-  if (cu > 0) {
-    const int64_t runs = std::min<int64_t>(std::max<int64_t>((cu + R - 1) / R, 1), nsplits);
-    spg = std::min<int32_t>(spg, (int32_t)((nsplits + runs - 1) / runs));
+  if (cu <= 0) return cap;
+  int32_t best = 1;
+  int64_t best_len = INT64_MAX;
+  for (int32_t spg = 1; spg <= cap; ++spg) {
+    const int64_t wgs = R * ((nsplits + spg - 1) / spg);
+    const int64_t len = (wgs + cu - 1) / cu * spg;
+    if (len <= best_len) {
+      best_len = len;
+      best = spg;
+    }
   }
-  return std::min(spg, nsplits);
+  return best;
 }
 
 bilogp_status check_on_device(const void* ptr, int dev, const char* name) {
