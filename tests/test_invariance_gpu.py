@@ -120,3 +120,37 @@ def test_layouts():
     assert torch.equal(lp3.reshape(-1), lp2) and torch.equal(ls3.reshape(-1), ls2)
     assert torch.equal(lpv, lp3) and torch.equal(lsv, ls3)
     assert torch.equal(lpe.reshape(-1), lpe2)
+
+
+_HEAD = {}
+
+
+def headline_full():
+    if "headline" not in _HEAD:
+        inp = synth.make_inputs("headline", device=DEV)
+        logp, lse = run_inputs(inp)
+        torch.cuda.synchronize()
+        _HEAD["headline"] = (inp, logp.reshape(-1), lse.reshape(-1))
+    return _HEAD["headline"]
+
+
+@pytest.mark.parametrize("rows", [768, 1280, 1792])
+def test_odd_row_block_counts_keep_the_bits(rows):
+    """V = 128256 (2 tiles per split).  The full 4096-row batch launches 16 row
+    blocks with runs of 2 splits; the first `rows` rows alone make an odd number
+    of 256-token blocks (3, 5, 7), for which whole rounds of the grid call for
+    runs of 1 split; 256-row chunks run 128-token blocks with three LDS
+    buffers.  Every one of them gives the full batch's bits."""
+    inp, full_lp, full_ls = headline_full()
+    h, t = flat(inp)
+    say(f"headline first {rows} rows: alone and in 256-row chunks vs the full batch")
+    lp, ls = run_ex(h[:rows], inp["weight"], t[:rows], inp["bias"])
+    lps, lss = [], []
+    for c0 in range(0, rows, 256):
+        a, b = run_ex(h[c0:c0 + 256], inp["weight"], t[c0:c0 + 256], inp["bias"])
+        lps.append(a)
+        lss.append(b)
+    torch.cuda.synchronize()
+    assert torch.equal(lp, full_lp[:rows]) and torch.equal(ls, full_ls[:rows])
+    assert torch.equal(torch.cat(lps), full_lp[:rows])
+    assert torch.equal(torch.cat(lss), full_ls[:rows])
