@@ -50,10 +50,12 @@
 // operand fragments of step u + 1 are read from LDS while the MFMAs of step
 // u run (two fragment sets in registers), so LDS latency - which grows while
 // the direct loads are writing LDS - stays off the MFMA path.  The stage's
-// barrier sits before step 3: once every wave has read step 3's operands
+// barrier sits inside step 3, after its first MFMAs (with 256-token blocks
+// two; their operands are already in registers, so the matrix core keeps
+// working while the wave waits): once every wave has read step 3's operands
 // and its loads of the next stage have landed, the buffer is released and
-// refilled with stage g + 2 - the W slice under the MFMAs of step 3, the
-// hidden slice under those of step 0 of stage g + 1.  Each of these steps
+// refilled with stage g + 2 - the W slice under the rest of step 3, the
+// hidden slice under the MFMAs of step 0 of stage g + 1.  Each of these steps
 // is emitted in a fixed order (MFMA, LDS read, and a direct load after every
 // second MFMA): the texture-address unit takes one 1 KB load about every 16
 // cycles, so a wave that issued its loads in one burst would sit at the load
@@ -381,6 +383,35 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // The last K step of a stage (two token columns per wave) with the stage
+  // barrier inside it: the first kPreBarrier MFMAs use fragments already in
+  // registers and keep the matrix core busy while the wave waits for the
+  // others; after the barrier the remaining six MFMAs each carry one read of
+  // the next stage's step-0 fragments (b0 a0 b1 a1 a2 a3), and the W slice of
+  // stage g + 2 is loaded into the released buffer after MFMAs 3, 4, 6 and 7.
+  // (Two MFMAs ahead of the barrier timed best on MI355X: 3.11 ms at the
+  // headline shape against 3.20 ms with one and 3.14 / 3.18 ms with three or
+  // four.)
+  auto step_bar = [&](const bf16x8 (&a)[4], const bf16x8 (&b)[kTi], const uint8_t* nst,
+                      bf16x8 (&na)[4], bf16x8 (&nb)[kTi], const LoadCtx& lc, auto sync) {
+    static_assert(kTi == 2, "two token columns per wave");
+    constexpr int kPreBarrier = 2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int vi = i / 2, ti = i % 2;
+      acc[vi][ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[vi], b[ti], acc[vi][ti], 0, 0, 0);
+      if (i == kPreBarrier - 1) sync();
+      if (i == 2) nb[0] = *(const bf16x8*)(nst + b_off[0]);
+      if (i == 3) na[0] = *(const bf16x8*)(nst + a_off[0]);
+      if (i == 4) nb[1] = *(const bf16x8*)(nst + b_off[0] + 32 * kLdsRowBytes);
+      if (i >= 5) na[i - 4] = *(const bf16x8*)(nst + a_off[0] + (i - 4) * 32 * kLdsRowBytes);
+      if (i == 3) load_one(lc, 0, std::false_type{});
+      if (i == 4) load_one(lc, 1, std::false_type{});
+      if (i == 6) load_one(lc, 2, std::false_type{});
+      if (i == 7) load_one(lc, 3, std::false_type{});
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   auto read_frags = [&](const uint8_t* st, int uu, bf16x8 (&a)[4], bf16x8 (&b)[kTi]) {
     b[0] = *(const bf16x8*)(st + b_off[uu]);
     a[0] = *(const bf16x8*)(st + a_off[uu]);
@@ -417,9 +448,13 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
     step(fa0, fb0, st, 1, fa1, fb1, lh, std::true_type{}, std::true_type{});
     step(fa1, fb1, st, 2, fa0, fb0, lh, std::false_type{}, std::true_type{});
     step(fa0, fb0, st, 3, fa1, fb1, lh, std::false_type{}, std::true_type{});
-    sync_stage();
     const LoadCtx lw = ctx_w(g + 2, sc);
-    step(fa1, fb1, slot_ptr(sn), 0, fa0, fb0, lw, std::true_type{}, std::false_type{});
+    if constexpr (kTi == 2) {
+      step_bar(fa1, fb1, slot_ptr(sn), fa0, fb0, lw, sync_stage);
+    } else {
+      sync_stage();
+      step(fa1, fb1, slot_ptr(sn), 0, fa0, fb0, lw, std::true_type{}, std::false_type{});
+    }
   };
   // Stage g with three buffers: SC holds stage g, SN stage g + 1 and SP (free
   // since the previous stage's barrier) receives the hidden slice of stage
