@@ -104,10 +104,11 @@ int32_t row_block_rows(int64_t N, int64_t splits, int dev) {
 // splits; the host takes the one whose grid, run in whole rounds of one
 // workgroup per compute unit, ends first: ceil(R * runs / CUs) rounds of that
 // many splits each (a grid that leaves units idle scores its idle share too);
-// ties go to the longer run (fewer workgroup starts).  (Measured on MI355X at H = 4096, V = 128256: runs of 4 tiles beat
-// runs of 2, 8, 16 or 32 from N = 256 up, or tie within 1%, where the rounds
-// come out even; with 3 row blocks, runs of 2 splits left half of the second
-// round idle and took 0.785 ms where runs of 1 split need 3 full rounds.)
+// ties go to the longer run (fewer workgroup starts).  (Measured on MI355X
+// at H = 4096, V = 128256: runs of 4 tiles beat runs of 2, 8, 16 or 32 from
+// N = 256 up, or tie within 1%, where the rounds come out even; with 3 row
+// blocks, runs of 2 splits left half of the second round idle and took
+// 0.80 ms where runs of 1 split, 3 full rounds, take 0.66 ms.)
 constexpr int kTilesPerRun = 4;
 
 int32_t splits_per_run(int64_t R, int nsplits, int vps, int dev) {

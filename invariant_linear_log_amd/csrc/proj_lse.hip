@@ -326,8 +326,11 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
 
   // The bias of tile v reaches LDS (bias_lds[v & 1]) by one direct load of
   // 1 KB from wave 0, issued in the epilogue of tile v - 1 once that tile's
-  // bias is consumed (tile 0: in the prologue); tile v's first stage barrier
-  // makes it visible.  The epilogue of tile v reads it from there: nothing
+  // bias is consumed (tile 0: in the prologue).  A stage barrier of tile v
+  // makes it visible: the first one with two buffers (it waits for every
+  // load); with three, where a barrier leaves the newest six loads in
+  // flight, the first one after six more loads - one or two stages on, long
+  // before the epilogue.  The epilogue of tile v reads it from there: nothing
   // bias-related runs in the stage loop, and no global load whose wait would
   // also wait for the next stages' prefetch (the load counter is in order).
   const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
@@ -430,9 +433,9 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
     wait_vmcnt<0>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
-  // Three buffers: the loads still allowed in flight are the W slice of the
-  // stage after next and the hidden slice of the next stage (issued after
-  // everything the next stage needs; the load counter completes in order).
+  // Three buffers: at stage g's barrier the loads still allowed in flight are
+  // the W and hidden slices of stage g + 2, issued after everything stage
+  // g + 1 needs (the load counter completes in order).
   auto sync_stage3 = [&]() {
     wait_vmcnt<kLoadsPerOperand + kLoadsH>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
