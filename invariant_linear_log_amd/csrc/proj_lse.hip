@@ -406,7 +406,7 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
       if (i == kPreBarrier - 1) sync();
       if (i == 2) nb[0] = *(const bf16x8*)(nst + b_off[0]);
       if (i == 3) na[0] = *(const bf16x8*)(nst + a_off[0]);
-      if (i == 4) nb[1] = *(const bf16x8*)(nst + b_off[0] + 32 * kLdsRowBytes);
+      if (i == 4) nb[kTi - 1] = *(const bf16x8*)(nst + b_off[0] + 32 * kLdsRowBytes);
       if (i >= 5) na[i - 4] = *(const bf16x8*)(nst + a_off[0] + (i - 4) * 32 * kLdsRowBytes);
       if (i == 3) load_one(lc, 0, std::false_type{});
       if (i == 4) load_one(lc, 1, std::false_type{});
