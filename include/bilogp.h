@@ -32,9 +32,16 @@
  *  - Asynchrony: all device work is enqueued on `stream` (a hipStream_t;
  *    NULL = the null stream).  No entry point synchronizes; inputs must stay
  *    alive until the stream reaches the work.
- *  - Errors: no entry point throws.  On any error nothing is launched and the
- *    outputs are left untouched; a status is returned and a thread-local
- *    message is available from bilogp_last_error().
+ *  - Errors: no entry point throws.  Every argument is checked before any
+ *    device work: on BILOGP_E_INVALID_ARG, _UNSUPPORTED or _WORKSPACE nothing
+ *    is launched and the outputs are left untouched.  BILOGP_E_HIP reports a
+ *    failure of the HIP runtime itself (a launch or allocation the checks
+ *    could not foresee); kernels of the same call enqueued before it may
+ *    still run.  A status is returned and a thread-local message is
+ *    available from bilogp_last_error().
+ *  - Grids: a call on any N the checks accept is issued as row chunks whose
+ *    grids fit the 32-bit work-item limit; rows are independent, so this
+ *    never changes a bit.
  *  - Failing closed (the page's registry maps unsupported platforms to an
  *    explicit error rather than a generic fallback): a device that is not
  *    gfx950 gives BILOGP_E_UNSUPPORTED; there is no other code path.
@@ -51,7 +58,29 @@
 extern "C" {
 #endif
 
-#define BILOGP_ABI_VERSION 1
+#define BILOGP_ABI_VERSION 2
+
+/* Version of the bit contract: for given inputs of one row (its hidden row
+ * and target, W, bias, H, V), which fp32 bits logp and lse take.  The page
+ * fixes no bits (several fp32 results are equally correct, PR #337
+ * description, "Why this happens"); what this library promises is that the
+ * bits of one version never depend on N, the row's position, the other rows,
+ * the stream or the compute units.  A change to anything that orders the
+ * arithmetic changes the version:
+ *   1  tiles of 256 columns, at most 64 splits; merge tree whose lanes
+ *      pre-summed strided splits
+ *   2  tiles of 256 columns, at most 256 splits; merge tree whose lanes
+ *      pre-sum consecutive splits (a perfect pairwise tree over ascending
+ *      split index); K reduced in ascending 16-wide steps of
+ *      v_mfma_f32_32x32x16_bf16; per token, each lane sums its 64 values of a
+ *      tile in a fixed register order, then the two lane halves and the two
+ *      vocabulary-half waves are merged in fixed operand order
+ *   3  as 2, but K is reduced in ascending 32-wide steps of
+ *      v_mfma_f32_16x16x32_bf16, and per token each lane sums its 32 values
+ *      of a tile (8 blocks of 4 vocabulary rows) in a fixed register order,
+ *      then the four lane groups (pairs 16 lanes apart, then 32 apart) and
+ *      the two vocabulary-half waves are merged in fixed operand order */
+#define BILOGP_BIT_CONTRACT_VERSION 3
 
 typedef enum bilogp_status {
   BILOGP_OK = 0,
@@ -70,6 +99,10 @@ typedef enum bilogp_bias_dtype {
 
 /* BILOGP_ABI_VERSION of the built library. */
 int bilogp_abi_version(void);
+
+/* BILOGP_BIT_CONTRACT_VERSION of the built library: outputs of two builds
+ * with the same value are bit-identical for the same inputs. */
+int bilogp_bit_contract_version(void);
 
 /* Width of a vocabulary tile in columns.  Part of the bit contract. */
 int bilogp_vtile_cols(void);
@@ -144,7 +177,7 @@ size_t bilogp_workspace_bytes_mode(int64_t N, int64_t V, int mode, int cu_count)
  *   lse_out  device, fp32 [N]   (written)
  *   0 <= N <= 2^32 (N == 0 is a successful no-op), 8 <= H <= 2^20 with
  *   H % 8 == 0, 1 <= V <= 2^30.  The outputs must not overlap each other, an
- *   input or the workspace.
+ *   input or the workspace; the workspace must not overlap an input.
  */
 bilogp_status bilogp_forward(const void* hidden, const void* weight, const int64_t* target,
                              const float* bias, float* logp_out, float* lse_out,
@@ -159,11 +192,21 @@ bilogp_status bilogp_forward_ex(const void* hidden, const void* weight, const in
                                 float* lse_out, int64_t N, int64_t H, int64_t V,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
-/* bilogp_forward_ex under split policy `mode` (BILOGP_SPLITS_INVARIANT gives
- * exactly bilogp_forward_ex).  cu_count >= 1 is the compute-unit count the
- * throughput policy fills (normally the device's); the workspace must hold
- * bilogp_workspace_bytes_mode(N, V, mode, cu_count) bytes.  An unknown mode,
- * or cu_count < 1 in throughput mode, gives BILOGP_E_INVALID_ARG.  At most
+/* bilogp_forward_ex under split policy `mode`, scheduled for `cu_count`
+ * compute units.
+ *
+ * cu_count is the compute-unit count the launch is scheduled for: the row-
+ * block height (256 or 128 tokens) and how many consecutive splits one
+ * workgroup takes.  0 means the current device's count.  In the invariant
+ * mode it is scheduling only: the bits are those of bilogp_forward_ex for
+ * every cu_count (that is the contract's "never on the number of compute
+ * units", and it lets a test vary the count on one device).  In the
+ * throughput mode it is also the count the split policy fills, so it must be
+ * >= 1 and the bits then depend on it.
+ *
+ * The workspace must hold bilogp_workspace_bytes_mode(N, V, mode, cu_count)
+ * bytes.  An unknown mode, cu_count outside [0, 65536], or cu_count < 1 in
+ * throughput mode gives BILOGP_E_INVALID_ARG.  At most
  * BILOGP_MAX_THROUGHPUT_SPLITS splits are combined, in ascending order. */
 bilogp_status bilogp_forward_mode(const void* hidden, const void* weight, const int64_t* target,
                                   const void* bias, int bias_dtype, float* logp_out,

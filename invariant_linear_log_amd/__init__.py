@@ -46,6 +46,7 @@ from ._binding import (  # noqa: F401
     BILOGP_GEMM_OUT_F32,
     BILOGP_GEMM_OUT_F32_ACCUM,
     bilogp_abi_version,
+    bilogp_bit_contract_version,
     bilogp_backward,
     bilogp_backward_workspace_bytes,
     bilogp_det_gemm_da,

@@ -43,6 +43,7 @@ _VP = ctypes.c_void_p
 _I64 = ctypes.c_int64
 SIGNATURES = {
     "bilogp_abi_version": (ctypes.c_int, []),
+    "bilogp_bit_contract_version": (ctypes.c_int, []),
     "bilogp_vtile_cols": (ctypes.c_int, []),
     "bilogp_max_splits": (ctypes.c_int, []),
     "bilogp_vtiles_per_split": (ctypes.c_int, [_I64]),
@@ -114,6 +115,68 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+# ---------------------------------------------------------------- argument checks
+# The library validates sizes, alignment, aliasing and devices, but it sees
+# only pointers: a tensor of the wrong dtype or shape would be read with the
+# wrong element size or past its end.  Each wrapper therefore checks what the
+# pointers stand for before it calls in (TypeError for a dtype, ValueError for
+# a shape, layout or device).
+def _tensor(t, name: str, dtypes, shape=None, ndim=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if not isinstance(dtypes, tuple):
+        dtypes = (dtypes,)
+    if t.dtype not in dtypes:
+        want = " or ".join(str(d) for d in dtypes)
+        raise TypeError(f"{name} must be {want}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D, got shape {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _workspace(ws, name: str = "workspace") -> None:
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(ws).__name__}")
+    if not ws.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _same_device(*tensors) -> None:
+    ts = [t for t in tensors if t is not None]
+    dev = ts[0].device
+    if dev.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, got {dev}")
+    for t in ts[1:]:
+        if t.device != dev:
+            raise ValueError(f"all tensors must be on {dev}, got one on {t.device}")
+
+
+def _forward_args(hidden, weight, target, bias, bias_dtypes, V=None, w_rows=None):
+    """Checks shared by the forward-style calls; returns (N, H, V)."""
+    _tensor(hidden, "hidden", torch.bfloat16, ndim=2)
+    N, H = hidden.shape
+    _tensor(weight, "weight", torch.bfloat16, ndim=2)
+    if weight.shape[1] != H:
+        raise ValueError(f"weight has {weight.shape[1]} columns, hidden has H = {H}")
+    if V is None:
+        V = weight.shape[0]
+    if w_rows is not None and weight.shape[0] != w_rows:
+        raise ValueError(f"weight slice has {weight.shape[0]} rows, the split range holds "
+                         f"{w_rows} vocabulary columns")
+    _tensor(target, "target", torch.int64, shape=(N,))
+    if bias is not None:
+        _tensor(bias, "bias", bias_dtypes, shape=(weight.shape[0],))
+    return N, H, V
+
+
+def _outputs(N: int, *outs) -> None:
+    for name, t in zip(("logp_out", "lse_out"), outs):
+        _tensor(t, name, torch.float32, shape=(N,))
+
+
 def _stream_handle(stream, device) -> int:
     if stream is None:
         stream = torch.cuda.current_stream(device)
@@ -125,6 +188,10 @@ def _stream_handle(stream, device) -> int:
 # ---------------------------------------------------------------- plain queries
 def bilogp_abi_version() -> int:
     return load_library().bilogp_abi_version()
+
+
+def bilogp_bit_contract_version() -> int:
+    return load_library().bilogp_bit_contract_version()
 
 
 def bilogp_vtile_cols() -> int:
@@ -184,8 +251,9 @@ def bilogp_forward(hidden: torch.Tensor, weight: torch.Tensor, target: torch.Ten
     """``bilogp_forward`` on 2-D contiguous device tensors (hidden [N, H] bf16,
     weight [V, H] bf16, target [N] int64, bias [V] fp32 or None, outputs [N]
     fp32).  The library allocates its workspace stream-ordered."""
-    N, H = hidden.shape
-    V = weight.shape[0]
+    N, H, V = _forward_args(hidden, weight, target, bias, torch.float32)
+    _outputs(N, logp_out, lse_out)
+    _same_device(hidden, weight, target, bias, logp_out, lse_out)
     lib = load_library()
     with torch.cuda.device(hidden.device):
         st = lib.bilogp_forward(_ptr(hidden), _ptr(weight), _ptr(target), _ptr(bias),
@@ -200,8 +268,11 @@ def bilogp_forward_ex(hidden: torch.Tensor, weight: torch.Tensor, target: torch.
                       stream=None) -> None:
     """``bilogp_forward_ex`` with a caller-owned workspace tensor (any dtype;
     its byte size is passed).  Allocates nothing."""
-    N, H = hidden.shape
-    V = weight.shape[0]
+    N, H, V = _forward_args(hidden, weight, target, bias, (torch.bfloat16, torch.float32))
+    _outputs(N, logp_out, lse_out)
+    if workspace is not None:
+        _workspace(workspace)
+    _same_device(hidden, weight, target, bias, logp_out, lse_out, workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     lib = load_library()
     with torch.cuda.device(hidden.device):
@@ -218,8 +289,11 @@ def bilogp_forward_mode(hidden: torch.Tensor, weight: torch.Tensor, target: torc
                         workspace: Optional[torch.Tensor], stream=None) -> None:
     """``bilogp_forward_mode``: ``bilogp_forward_ex`` under split policy
     ``mode`` with ``cu_count`` compute units for the throughput policy."""
-    N, H = hidden.shape
-    V = weight.shape[0]
+    N, H, V = _forward_args(hidden, weight, target, bias, (torch.bfloat16, torch.float32))
+    _outputs(N, logp_out, lse_out)
+    if workspace is not None:
+        _workspace(workspace)
+    _same_device(hidden, weight, target, bias, logp_out, lse_out, workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     lib = load_library()
     with torch.cuda.device(hidden.device):
@@ -234,8 +308,9 @@ def bilogp_partials(hidden: torch.Tensor, weight: torch.Tensor, target: torch.Te
                     bias: Optional[torch.Tensor], workspace: torch.Tensor, stream=None) -> None:
     """``bilogp_partials``: projection + per-split online softmax into the
     workspace (partials and target logits)."""
-    N, H = hidden.shape
-    V = weight.shape[0]
+    N, H, V = _forward_args(hidden, weight, target, bias, (torch.bfloat16, torch.float32))
+    _workspace(workspace)
+    _same_device(hidden, weight, target, bias, workspace)
     lib = load_library()
     with torch.cuda.device(hidden.device):
         st = lib.bilogp_partials(_ptr(hidden), _ptr(weight), _ptr(target), _ptr(bias),
@@ -251,7 +326,17 @@ def bilogp_partials_range(hidden: torch.Tensor, weight_slice: torch.Tensor,
                           stream=None) -> None:
     """``bilogp_partials_range``: partials of splits [split_begin, split_end)
     of the full vocabulary V from that range's weight (and bias) columns."""
-    N, H = hidden.shape
+    S = bilogp_num_vocab_splits(V)
+    if S == 0:
+        raise ValueError(f"V = {V} out of range")
+    if not (0 <= split_begin < split_end <= S):
+        raise ValueError(f"split range must satisfy 0 <= begin < end <= {S}, got "
+                         f"[{split_begin}, {split_end})")
+    c0, c1 = vocab_split_columns(V, split_begin, split_end)
+    N, H, _ = _forward_args(hidden, weight_slice, target, bias_slice,
+                            (torch.bfloat16, torch.float32), V=V, w_rows=c1 - c0)
+    _workspace(workspace)
+    _same_device(hidden, weight_slice, target, bias_slice, workspace)
     lib = load_library()
     with torch.cuda.device(hidden.device):
         st = lib.bilogp_partials_range(_ptr(hidden), _ptr(weight_slice), _ptr(target),
@@ -274,7 +359,11 @@ def vocab_split_columns(V: int, split_begin: int, split_end: int):
 def bilogp_merge(target: torch.Tensor, workspace: torch.Tensor, logp_out: torch.Tensor,
                  lse_out: torch.Tensor, V: int, stream=None) -> None:
     """``bilogp_merge``: ascending combine of the workspace partials."""
+    _tensor(target, "target", torch.int64, ndim=1)
     N = target.shape[0]
+    _outputs(N, logp_out, lse_out)
+    _workspace(workspace)
+    _same_device(target, workspace, logp_out, lse_out)
     lib = load_library()
     with torch.cuda.device(target.device):
         st = lib.bilogp_merge(_ptr(target), _ptr(workspace),
@@ -297,8 +386,14 @@ def _gemm_kind(out: torch.Tensor, accumulate: bool) -> int:
 def bilogp_det_gemm_fwd(a: torch.Tensor, b: torch.Tensor, c: torch.Tensor,
                         accumulate: bool = False, stream=None) -> None:
     """``bilogp_det_gemm_fwd``: c[M, N] (=|+=) a[M, K] . b[N, K]^T."""
+    _tensor(a, "a", torch.bfloat16, ndim=2)
     M, K = a.shape
+    _tensor(b, "b", torch.bfloat16, ndim=2)
+    if b.shape[1] != K:
+        raise ValueError(f"b has {b.shape[1]} columns, a has K = {K}")
     N = b.shape[0]
+    _tensor(c, "c", (torch.bfloat16, torch.float32), shape=(M, N))
+    _same_device(a, b, c)
     with torch.cuda.device(a.device):
         st = load_library().bilogp_det_gemm_fwd(_ptr(a), _ptr(b), _ptr(c), M, N, K,
                                                 _gemm_kind(c, accumulate),
@@ -309,8 +404,14 @@ def bilogp_det_gemm_fwd(a: torch.Tensor, b: torch.Tensor, c: torch.Tensor,
 def bilogp_det_gemm_da(dc: torch.Tensor, b: torch.Tensor, da: torch.Tensor,
                        accumulate: bool = False, stream=None) -> None:
     """``bilogp_det_gemm_da``: da[M, K] (=|+=) dc[M, N] . b[N, K]."""
+    _tensor(dc, "dc", torch.bfloat16, ndim=2)
     M, N = dc.shape
+    _tensor(b, "b", torch.bfloat16, ndim=2)
+    if b.shape[0] != N:
+        raise ValueError(f"b has {b.shape[0]} rows, dc has N = {N}")
     K = b.shape[1]
+    _tensor(da, "da", (torch.bfloat16, torch.float32), shape=(M, K))
+    _same_device(dc, b, da)
     with torch.cuda.device(dc.device):
         st = load_library().bilogp_det_gemm_da(_ptr(dc), _ptr(b), _ptr(da), M, N, K,
                                                _gemm_kind(da, accumulate),
@@ -321,8 +422,14 @@ def bilogp_det_gemm_da(dc: torch.Tensor, b: torch.Tensor, da: torch.Tensor,
 def bilogp_det_gemm_db(a: torch.Tensor, dc: torch.Tensor, db: torch.Tensor,
                        accumulate: bool = False, stream=None) -> None:
     """``bilogp_det_gemm_db``: db[N, K] (=|+=) dc[M, N]^T . a[M, K]."""
+    _tensor(a, "a", torch.bfloat16, ndim=2)
     M, K = a.shape
+    _tensor(dc, "dc", torch.bfloat16, ndim=2)
+    if dc.shape[0] != M:
+        raise ValueError(f"dc has {dc.shape[0]} rows, a has M = {M}")
     N = dc.shape[1]
+    _tensor(db, "db", (torch.bfloat16, torch.float32), shape=(N, K))
+    _same_device(a, dc, db)
     with torch.cuda.device(a.device):
         st = load_library().bilogp_det_gemm_db(_ptr(a), _ptr(dc), _ptr(db), M, N, K,
                                                _gemm_kind(db, accumulate),
@@ -344,8 +451,16 @@ def bilogp_backward(hidden: torch.Tensor, weight: torch.Tensor, target: torch.Te
     weight [V, H] bf16, target [N] int64, bias [V] or None, lse / grad_logp /
     grad_lse [N] fp32; writes grad_hidden [N, H], grad_weight [V, H] and
     grad_bias [V] (fp32, grad_bias optional)."""
-    N, H = hidden.shape
-    V = weight.shape[0]
+    N, H, V = _forward_args(hidden, weight, target, bias, (torch.bfloat16, torch.float32))
+    for name, t in (("lse", lse), ("grad_logp", grad_logp), ("grad_lse", grad_lse)):
+        _tensor(t, name, torch.float32, shape=(N,))
+    _tensor(grad_hidden, "grad_hidden", torch.float32, shape=(N, H))
+    _tensor(grad_weight, "grad_weight", torch.float32, shape=(V, H))
+    if grad_bias is not None:
+        _tensor(grad_bias, "grad_bias", torch.float32, shape=(V,))
+    _workspace(workspace)
+    _same_device(hidden, weight, target, bias, lse, grad_logp, grad_lse, grad_hidden,
+                 grad_weight, grad_bias, workspace)
     ws_bytes = workspace.numel() * workspace.element_size()
     lib = load_library()
     with torch.cuda.device(weight.device):

@@ -33,6 +33,7 @@ bilogp_status fail(bilogp_status st, const std::string& msg) {
 constexpr int64_t kMaxV = int64_t(1) << 30;
 constexpr int64_t kMaxH = int64_t(1) << 20;
 constexpr int64_t kMaxN = int64_t(1) << 32;
+constexpr int kMaxCuCount = 65536;
 constexpr size_t kAlign = 256;
 
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -89,11 +90,10 @@ bilogp_status check_device(int* dev_out) {
 }
 
 // Row-block height of a projection launch: 256 tokens, or 128 when 256-token
-// blocks give fewer workgroups than the device has compute units.  A row's
-// arithmetic is the same in either (row blocking never changes bits), so the
-// choice may follow N and the device.
-int32_t row_block_rows(int64_t N, int64_t splits, int dev) {
-  const int cu = g_cu_count[dev].load(std::memory_order_acquire);
+// blocks give fewer workgroups than `cu` compute units.  A row's arithmetic
+// is the same in either (row blocking never changes bits), so the choice may
+// follow N and the device.
+int32_t row_block_rows(int64_t N, int64_t splits, int cu) {
   const int64_t r256 = (N + 255) / 256;
   return (cu > 0 && r256 * splits < cu) ? 128 : 256;
 }
@@ -102,7 +102,7 @@ int32_t row_block_rows(int64_t N, int64_t splits, int dev) {
 // each split's partial is written by the same arithmetic however the splits
 // are grouped.  Candidates are 1 .. about kTilesPerRun tiles' worth of
 // splits; the host takes the one whose grid, run in whole rounds of one
-// workgroup per compute unit, ends first: ceil(R * runs / CUs) rounds of that
+// workgroup per compute unit, ends first: ceil(R * runs / cu) rounds of that
 // many splits each (a grid that leaves units idle scores its idle share too);
 // ties go to the longer run (fewer workgroup starts).  (Measured on MI355X
 // at H = 4096, V = 128256: runs of 4 tiles beat runs of 2, 8, 16 or 32 from
@@ -111,10 +111,9 @@ int32_t row_block_rows(int64_t N, int64_t splits, int dev) {
 // 0.80 ms where runs of 1 split, 3 full rounds, take 0.66 ms.)
 constexpr int kTilesPerRun = 4;
 
-int32_t splits_per_run(int64_t R, int nsplits, int vps, int dev) {
+int32_t splits_per_run(int64_t R, int nsplits, int vps, int cu) {
   if (nsplits <= 1) return 1;
   const int32_t cap = std::min(std::max(1, kTilesPerRun / std::max(vps, 1)), nsplits);
-  const int cu = g_cu_count[dev].load(std::memory_order_acquire);
   if (cu <= 0) return cap;
   int32_t best = 1;
   int64_t best_len = INT64_MAX;
@@ -128,6 +127,8 @@ int32_t splits_per_run(int64_t R, int nsplits, int vps, int dev) {
   }
   return best;
 }
+
+int device_cus(int dev) { return g_cu_count[dev].load(std::memory_order_acquire); }
 
 bilogp_status check_on_device(const void* ptr, int dev, const char* name) {
   hipPointerAttribute_t attr;
@@ -159,6 +160,8 @@ Range range_of(const void* p, size_t bytes) {
 extern "C" {
 
 int bilogp_abi_version(void) { return BILOGP_ABI_VERSION; }
+
+int bilogp_bit_contract_version(void) { return BILOGP_BIT_CONTRACT_VERSION; }
 
 int bilogp_vtile_cols(void) { return bilogp::kVtileCols; }
 
@@ -264,6 +267,8 @@ bilogp_status validate(const Call& c, int parts, bilogp::ProjParams* out) {
     return fail(BILOGP_E_INVALID_ARG, "unknown split mode");
   if (c.mode == BILOGP_SPLITS_THROUGHPUT && c.cu_count < 1)
     return fail(BILOGP_E_INVALID_ARG, "the throughput split mode needs cu_count >= 1");
+  if (c.cu_count < 0 || c.cu_count > kMaxCuCount)
+    return fail(BILOGP_E_INVALID_ARG, "cu_count out of range [0, 65536]");
   size_t bias_esz = 0;
   if (proj) {
     if (c.bias_dtype != BILOGP_BIAS_NONE && c.bias_dtype != BILOGP_BIAS_BF16 &&
@@ -318,6 +323,20 @@ bilogp_status validate(const Call& c, int parts, bilogp::ProjParams* out) {
     return fail(BILOGP_E_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
   if (reinterpret_cast<uintptr_t>(c.ws) % kAlign != 0)
     return fail(BILOGP_E_WORKSPACE, "workspace must be 256-byte aligned");
+  {
+    // the projection writes the workspace while it reads the inputs: they
+    // must not share a byte (checked for every part, so a workspace is never
+    // an input of any call)
+    const Range r_ws = range_of(c.ws, c.ws_bytes);
+    const Range ins[] = {
+        proj ? range_of(c.hidden, (size_t)c.N * c.H * 2) : Range{0, 0},
+        proj ? range_of(c.weight, (size_t)(col1 - col0) * c.H * 2) : Range{0, 0},
+        range_of(c.target, (size_t)c.N * 8),
+        (proj && c.bias) ? range_of(c.bias, (size_t)(col1 - col0) * bias_esz) : Range{0, 0}};
+    for (const Range& in : ins)
+      if (overlap(r_ws, in))
+        return fail(BILOGP_E_INVALID_ARG, "the workspace overlaps an input");
+  }
 
   int dev = -1;
   bilogp_status st = check_device(&dev);
@@ -334,7 +353,10 @@ bilogp_status validate(const Call& c, int parts, bilogp::ProjParams* out) {
 
   const WsLayout L = ws_layout(c.ws, c.N, S);
   bilogp::ProjParams& p = *out;
-  p.rows = row_block_rows(c.N, ranged ? c.split_end - c.split_begin : S, dev);
+  // compute units the launch is scheduled for: the caller's count, else the
+  // device's (row blocking and split runs never change a bit)
+  const int cu = c.cu_count > 0 ? c.cu_count : device_cus(dev);
+  p.rows = row_block_rows(c.N, ranged ? c.split_end - c.split_begin : S, cu);
   p.hidden = c.hidden;
   // absolute-column addressing: shift the slice's base back by col0 columns
   // (unsigned arithmetic; the kernel adds them again before any access)
@@ -358,18 +380,25 @@ bilogp_status validate(const Call& c, int parts, bilogp::ProjParams* out) {
   p.R = (int32_t)((c.N + p.rows - 1) / p.rows);
   p.split0 = ranged ? c.split_begin : 0;
   p.split1 = ranged ? c.split_end : S;
-  p.spg = splits_per_run(p.R, p.split1 - p.split0, p.vps, dev);
+  p.spg = splits_per_run(p.R, p.split1 - p.split0, p.vps, cu);
   p.S_grid = (p.split1 - p.split0 + p.spg - 1) / p.spg;
-  if ((int64_t)p.R * p.S_grid > INT32_MAX)    // unreachable: runs shrink as R grows
-    return fail(BILOGP_E_INVALID_ARG, "N too large for one launch");
   p.col0 = col0;
   return BILOGP_OK;
 }
 
+// Every grid stays within 32-bit work-item counts: the projection and the
+// merge are issued in row chunks.  Rows are independent and a row's
+// arithmetic does not depend on the rows around it, so chunking never changes
+// a bit.  Projection: 512 work-items per workgroup, S_grid workgroups per row
+// block.  Merge: 64 work-items per row.
+int64_t proj_chunk_rows(const bilogp::ProjParams& p) {
+  const int64_t max_blocks = (int64_t)(UINT32_MAX / 512u);
+  return std::max<int64_t>(1, max_blocks / std::max(p.S_grid, 1)) * p.rows;
+}
+constexpr int64_t kMergeChunkRows = int64_t(1) << 25;
+
 bilogp_status launch(const bilogp::ProjParams& p, const Call& c, int parts, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* logp = c.logp;
-  float* lse = c.lse;
   if ((parts & kProj) && c.bias) {
     // the padded fp32 copy of the bias columns the launch reads, from col0
     const int64_t cols = c.split_end >= 0
@@ -383,14 +412,28 @@ bilogp_status launch(const bilogp::ProjParams& p, const Call& c, int parts, void
       return fail(BILOGP_E_HIP, std::string("bias copy launch: ") + hipGetErrorString(e));
   }
   if (parts & kProj) {
-    hipError_t e = bilogp::launch_proj_lse(p, s);
-    if (e != hipSuccess)
-      return fail(BILOGP_E_HIP, std::string("projection launch: ") + hipGetErrorString(e));
+    const int64_t chunk = proj_chunk_rows(p);
+    for (int64_t r0 = 0; r0 < p.N; r0 += chunk) {
+      bilogp::ProjParams q = p;
+      q.N = std::min(chunk, p.N - r0);
+      q.R = (int32_t)((q.N + p.rows - 1) / p.rows);
+      q.hidden = static_cast<const uint16_t*>(p.hidden) + r0 * p.H;
+      q.target = p.target + r0;
+      q.part = p.part + r0 * p.S;
+      q.tlogit = p.tlogit + r0;
+      hipError_t e = bilogp::launch_proj_lse(q, s);
+      if (e != hipSuccess)
+        return fail(BILOGP_E_HIP, std::string("projection launch: ") + hipGetErrorString(e));
+    }
   }
   if (parts & kMerge) {
-    hipError_t e = bilogp::launch_merge(p.part, p.tlogit, p.target, logp, lse, p.N, p.S, p.V, s);
-    if (e != hipSuccess)
-      return fail(BILOGP_E_HIP, std::string("merge launch: ") + hipGetErrorString(e));
+    for (int64_t r0 = 0; r0 < p.N; r0 += kMergeChunkRows) {
+      const int64_t n = std::min(kMergeChunkRows, p.N - r0);
+      hipError_t e = bilogp::launch_merge(p.part + r0 * p.S, p.tlogit + r0, p.target + r0,
+                                          c.logp + r0, c.lse + r0, n, p.S, p.V, s);
+      if (e != hipSuccess)
+        return fail(BILOGP_E_HIP, std::string("merge launch: ") + hipGetErrorString(e));
+    }
   }
   return BILOGP_OK;
 }
@@ -547,7 +590,7 @@ bilogp_status gemm_run(const GemmCall& c, int64_t M, int64_t N, int64_t K, void*
   g.out_kind = c.out_kind;
   g.Pt = (int32_t)((c.P + 255) / 256);
   g.Qt = (int32_t)((c.Q + 255) / 256);
-  g.cu_count = g_cu_count[dev].load(std::memory_order_acquire);
+  g.cu_count = device_cus(dev);
   if ((int64_t)g.Pt * g.Qt > INT32_MAX) return fail(BILOGP_E_INVALID_ARG, "too many tiles");
   hipError_t e = bilogp::launch_det_gemm(g, c.xt, c.yt, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(BILOGP_E_HIP, std::string("gemm launch: ") + hipGetErrorString(e));
@@ -693,11 +736,11 @@ bilogp_status bilogp_backward(const void* hidden, const void* weight, const int6
       p.T = (int32_t)((V + bilogp::kVtileCols - 1) / bilogp::kVtileCols);
       p.vps = bilogp_vtiles_per_split(V);
       p.S = bilogp_num_vocab_splits(V);
-      p.rows = row_block_rows(N, p.S, dev);
+      p.rows = row_block_rows(N, p.S, device_cus(dev));
       p.R = (int32_t)((N + p.rows - 1) / p.rows);
       p.split0 = 0;
       p.split1 = p.S;
-      p.spg = splits_per_run(p.R, p.S, p.vps, dev);
+      p.spg = splits_per_run(p.R, p.S, p.vps, device_cus(dev));
       p.S_grid = (p.S + p.spg - 1) / p.spg;
       p.col0 = 0;
       p.lse = lse;
@@ -713,7 +756,7 @@ bilogp_status bilogp_backward(const void* hidden, const void* weight, const int6
       g.x = weight; g.y = dzt; g.out = grad_hidden;
       g.P = H; g.Q = N; g.C = V; g.ldx = H; g.ldy = ldz; g.ldo = H;
       g.out_kind = bilogp::kGemmF32;
-      g.cu_count = g_cu_count[dev].load(std::memory_order_acquire);
+      g.cu_count = device_cus(dev);
       g.Pt = (int32_t)((H + 255) / 256);
       g.Qt = (int32_t)((N + 255) / 256);
       e = bilogp::launch_det_gemm(g, true, true, s);
@@ -725,7 +768,7 @@ bilogp_status bilogp_backward(const void* hidden, const void* weight, const int6
     g.x = hidden; g.y = dzt; g.out = grad_weight;
     g.P = H; g.Q = V; g.C = N; g.ldx = H; g.ldy = ldz; g.ldo = H;
     g.out_kind = bilogp::kGemmF32;
-    g.cu_count = g_cu_count[dev].load(std::memory_order_acquire);
+    g.cu_count = device_cus(dev);
     g.Pt = (int32_t)((H + 255) / 256);
     g.Qt = (int32_t)((V + 255) / 256);
     e = bilogp::launch_det_gemm(g, true, false, s);

@@ -686,12 +686,6 @@ __device__ __forceinline__ void proj_lse_body(const ProjParams& p) {
   wait_vmcnt<0>();
 }
 
-__global__ __launch_bounds__(kThreads, 1) void proj_lse_kernel(const ProjParams p) {
-  proj_lse_body<false, false, 2>(p);
-}
-__global__ __launch_bounds__(kThreads, 1) void proj_lse_bias_kernel(const ProjParams p) {
-  proj_lse_body<true, false, 2>(p);
-}
 __global__ __launch_bounds__(kThreads, 1) void softmax_grad_kernel(const ProjParams p) {
   proj_lse_body<false, true, 2>(p);
 }
@@ -700,12 +694,6 @@ __global__ __launch_bounds__(kThreads, 1) void softmax_grad_bias_kernel(const Pr
 }
 // 128-token row blocks: twice the workgroups for batches that 256-token
 // blocks cannot spread over every compute unit; the same bits
-__global__ __launch_bounds__(kThreads, 1) void proj_lse_r128_kernel(const ProjParams p) {
-  proj_lse_body<false, false, 1, 3>(p);
-}
-__global__ __launch_bounds__(kThreads, 1) void proj_lse_bias_r128_kernel(const ProjParams p) {
-  proj_lse_body<true, false, 1, 3>(p);
-}
 __global__ __launch_bounds__(kThreads, 1) void softmax_grad_r128_kernel(const ProjParams p) {
   proj_lse_body<false, true, 1>(p);
 }
@@ -788,16 +776,6 @@ hipError_t launch_row_sums(const uint16_t* dzt, int64_t rows, int64_t N, int64_t
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(row_sums_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, dzt,
                      rows, N, ldz, out);
-  return hipGetLastError();
-}
-
-hipError_t launch_proj_lse(const ProjParams& p, hipStream_t stream) {
-  const int64_t blocks = (int64_t)p.R * p.S_grid;
-  if (blocks <= 0) return hipSuccess;
-  const bool bias = p.bias_kind != kBiasNone;
-  auto k = p.rows == 128 ? (bias ? proj_lse_bias_r128_kernel : proj_lse_r128_kernel)
-                         : (bias ? proj_lse_bias_kernel : proj_lse_kernel);
-  hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -35,7 +35,14 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_constants_and_version():
-    assert ila.bilogp_abi_version() == 1
+    # ABI 2 added bilogp_bit_contract_version and the scheduling compute-unit
+    # count of the invariant mode.  Bit contract 2: tiles of 256 columns, at
+    # most 256 splits, the merge tree over consecutive per-lane split blocks
+    # (contract 1 had at most 64 splits and lane-strided pre-sums).  Bit
+    # contract 3: K in 32-wide steps of the 16 x 16 x 32 bf16 MFMA, per-token
+    # sums over (lane group, register) of that tile layout.
+    assert ila.bilogp_abi_version() == 2
+    assert ila.bilogp_bit_contract_version() == 3
     assert ila.bilogp_vtile_cols() == 256
     assert ila.bilogp_max_splits() == 256
     for s in range(5):
@@ -158,6 +165,11 @@ def _call_ex(hidden=FAKE, weight=FAKE + 0x100000, target=FAKE + 0x200000, bias=N
     (dict(ws=None), B.BILOGP_E_WORKSPACE),
     (dict(ws_bytes=100), B.BILOGP_E_WORKSPACE),
     (dict(ws=FAKE + 0x500010), B.BILOGP_E_WORKSPACE),         # misaligned workspace
+    (dict(ws=FAKE), B.BILOGP_E_INVALID_ARG),                  # workspace over hidden
+    (dict(ws=FAKE + 0x100000), B.BILOGP_E_INVALID_ARG),       # workspace over weight
+    (dict(ws=FAKE + 0x1fff00), B.BILOGP_E_INVALID_ARG),       # workspace over target
+    (dict(bias_dtype=2, bias=FAKE + 0x600000, ws=FAKE + 0x5fff00,
+          ws_bytes=0x2000), B.BILOGP_E_INVALID_ARG),          # workspace over bias
 ])
 def test_forward_ex_fails_closed(kw, status):
     st = _call_ex(**kw)
@@ -177,6 +189,31 @@ def test_forward_mode_fails_closed(mode, cu, status):
                                  FAKE + 0x400000, 8, 64, 1000, mode, cu, FAKE + 0x500000, 1 << 20,
                                  None)
     assert st == status, (st, ila.bilogp_last_error())
+
+
+@pytest.mark.parametrize("cu", [-1, 65537, 1 << 30])
+def test_forward_mode_rejects_bad_compute_unit_counts(cu):
+    lib = ila.load_library()
+    for mode in (B.BILOGP_SPLITS_INVARIANT, B.BILOGP_SPLITS_THROUGHPUT):
+        st = lib.bilogp_forward_mode(FAKE, FAKE + 0x100000, FAKE + 0x200000, None, 0,
+                                     FAKE + 0x300000, FAKE + 0x400000, 8, 64, 1000, mode, cu,
+                                     FAKE + 0x500000, 1 << 20, None)
+        assert st == B.BILOGP_E_INVALID_ARG, (mode, cu, st, ila.bilogp_last_error())
+
+
+def test_workspace_may_not_alias_inputs_of_either_half():
+    lib = ila.load_library()
+    # projection only: the workspace written over hidden / target
+    st = lib.bilogp_partials(FAKE, FAKE + 0x100000, FAKE + 0x200000, None, 0, 8, 64, 1000,
+                             FAKE, 1 << 20, None)
+    assert st == B.BILOGP_E_INVALID_ARG, ila.bilogp_last_error()
+    st = lib.bilogp_partials_range(FAKE, FAKE + 0x100000, FAKE + 0x200000, None, 0, 8, 64,
+                                   128256, 0, 2, FAKE + 0x1fff00, 1 << 20, None)
+    assert st == B.BILOGP_E_INVALID_ARG, ila.bilogp_last_error()
+    # merge only: the workspace read over the targets
+    st = lib.bilogp_merge(FAKE + 0x200000, FAKE + 0x1fff00, 1 << 20, FAKE + 0x300000 + 0x100000,
+                          FAKE + 0x400000 + 0x100000, 8, 1000, None)
+    assert st == B.BILOGP_E_INVALID_ARG, ila.bilogp_last_error()
 
 
 def test_forward_mode_workspace_is_per_mode():
@@ -245,6 +282,84 @@ def test_wrapper_rejects_bad_inputs(case):
         b, exc = torch.zeros(100, dtype=torch.float64), TypeError
     with pytest.raises(exc):
         ila.forward(h, w, t, b)
+
+
+def _cpu_forward_args(N=4, H=16, V=40):
+    return dict(hidden=torch.zeros(N, H, dtype=torch.bfloat16),
+                weight=torch.zeros(V, H, dtype=torch.bfloat16),
+                target=torch.zeros(N, dtype=torch.int64), bias=None,
+                logp_out=torch.zeros(N), lse_out=torch.zeros(N))
+
+
+@pytest.mark.parametrize("fn", ["bilogp_forward", "bilogp_forward_ex", "bilogp_forward_mode"])
+@pytest.mark.parametrize("case,exc", [
+    ("hidden_fp32", TypeError), ("target_int32", TypeError), ("bias_bf16_plain", TypeError),
+    ("bias_fp64", TypeError), ("hidden_3d", ValueError), ("hidden_noncontig", ValueError),
+    ("weight_cols", ValueError), ("target_short", ValueError), ("bias_short", ValueError),
+    ("logp_short", ValueError), ("lse_fp64", TypeError), ("cpu", ValueError)])
+def test_raw_wrappers_check_what_pointers_stand_for(fn, case, exc):
+    """The C-ABI wrappers check dtypes, shapes and layout before the library
+    sees bare pointers (a bf16 bias read as fp32, an int32 target or a short
+    output would otherwise be read or written out of bounds)."""
+    a = _cpu_forward_args()
+    if case == "hidden_fp32":
+        a["hidden"] = a["hidden"].float()
+    elif case == "target_int32":
+        a["target"] = a["target"].int()
+    elif case == "bias_bf16_plain":
+        if fn != "bilogp_forward":
+            pytest.skip("bf16 bias is valid for the calls with an explicit bias dtype")
+        a["bias"] = torch.zeros(40, dtype=torch.bfloat16)
+    elif case == "bias_fp64":
+        a["bias"] = torch.zeros(40, dtype=torch.float64)
+    elif case == "hidden_3d":
+        a["hidden"] = a["hidden"].reshape(2, 2, 16)
+    elif case == "hidden_noncontig":
+        a["hidden"] = torch.zeros(16, 4, dtype=torch.bfloat16).t()
+    elif case == "weight_cols":
+        a["weight"] = torch.zeros(40, 24, dtype=torch.bfloat16)
+    elif case == "target_short":
+        a["target"] = a["target"][:3]
+    elif case == "bias_short":
+        a["bias"] = torch.zeros(39)
+    elif case == "logp_short":
+        a["logp_out"] = torch.zeros(3)
+    elif case == "lse_fp64":
+        a["lse_out"] = a["lse_out"].double()
+    args = [a["hidden"], a["weight"], a["target"], a["bias"], a["logp_out"], a["lse_out"]]
+    with pytest.raises(exc):
+        if fn == "bilogp_forward":
+            ila.bilogp_forward(*args)
+        elif fn == "bilogp_forward_ex":
+            ila.bilogp_forward_ex(*args, torch.zeros(1 << 16, dtype=torch.uint8))
+        else:
+            ila.bilogp_forward_mode(*args, B.BILOGP_SPLITS_INVARIANT, 0,
+                                    torch.zeros(1 << 16, dtype=torch.uint8))
+
+
+def test_raw_wrappers_partials_range_and_merge_checks():
+    a = _cpu_forward_args(V=128256)
+    ws = torch.zeros(1 << 16, dtype=torch.uint8)
+    # splits [0, 2) of V = 128256 hold columns [0, 1024): a slice of 1000 rows
+    # would be read past its end
+    with pytest.raises(ValueError, match="slice"):
+        ila.bilogp_partials_range(a["hidden"], torch.zeros(1000, 16, dtype=torch.bfloat16),
+                                  a["target"], None, 128256, 0, 2, ws)
+    with pytest.raises(ValueError, match="split range"):
+        ila.bilogp_partials_range(a["hidden"], torch.zeros(1024, 16, dtype=torch.bfloat16),
+                                  a["target"], None, 128256, 3, 2, ws)
+    with pytest.raises(ValueError, match="shape"):
+        ila.bilogp_partials_range(a["hidden"], torch.zeros(1024, 16, dtype=torch.bfloat16),
+                                  a["target"], torch.zeros(1000), 128256, 0, 2, ws)
+    with pytest.raises(ValueError, match="GPU"):     # right shapes, but host tensors
+        ila.bilogp_partials_range(a["hidden"], torch.zeros(1024, 16, dtype=torch.bfloat16),
+                                  a["target"], None, 128256, 0, 2, ws)
+    with pytest.raises(TypeError):
+        ila.bilogp_merge(a["target"].int(), ws, a["logp_out"], a["lse_out"], 128256)
+    with pytest.raises(ValueError):
+        ila.bilogp_merge(a["target"], ws, a["logp_out"][:2], a["lse_out"], 128256)
+    with pytest.raises(TypeError):
+        ila.bilogp_partials(a["hidden"], a["weight"], a["target"], None, ws.numpy())
 
 
 def test_binding_raises_when_library_missing(tmp_path):
