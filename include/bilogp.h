@@ -192,6 +192,25 @@ bilogp_status bilogp_forward_ex(const void* hidden, const void* weight, const in
                                 float* lse_out, int64_t N, int64_t H, int64_t V,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory - code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the forward
+ * of bilogp_forward_ex (same arguments and checks, same bits) with no
+ * workspace argument and no allocation of any kind.  The workspace is a
+ * library-owned device array of bilogp_noalloc_max_workspace_bytes() bytes
+ * (64 MiB), one per GPU, held until the process ends; a call whose
+ * bilogp_workspace_bytes(N, V) exceeds it fails with BILOGP_E_WORKSPACE
+ * before any device work (at V = 128256: beyond about 33,000 rows).  Every call
+ * on one GPU shares that GPU's array, and the array keeps the last call's
+ * contents (nothing in it needs to start at zero): calls that may overlap on
+ * one GPU - on different streams, or from several threads - race; serialize
+ * them, or use bilogp_forward_ex with a workspace per stream. */
+size_t bilogp_noalloc_max_workspace_bytes(void);
+
+bilogp_status bilogp_forward_noalloc(const void* hidden, const void* weight,
+                                     const int64_t* target, const void* bias, int bias_dtype,
+                                     float* logp_out, float* lse_out, int64_t N, int64_t H,
+                                     int64_t V, void* stream);
+
 /* bilogp_forward_ex under split policy `mode`, scheduled for `cu_count`
  * compute units.
  *

@@ -55,9 +55,11 @@ from ._binding import (  # noqa: F401
     bilogp_forward,
     bilogp_forward_ex,
     bilogp_forward_mode,
+    bilogp_forward_noalloc,
     bilogp_last_error,
     bilogp_max_splits,
     bilogp_merge,
+    bilogp_noalloc_max_workspace_bytes,
     bilogp_num_vocab_splits,
     bilogp_num_vocab_splits_mode,
     bilogp_partials,

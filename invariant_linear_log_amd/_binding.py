@@ -56,6 +56,9 @@ SIGNATURES = {
                                            _I64, ctypes.c_int, ctypes.c_int, _VP,
                                            ctypes.c_size_t, _VP]),
     "bilogp_forward": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _VP]),
+    "bilogp_noalloc_max_workspace_bytes": (ctypes.c_size_t, []),
+    "bilogp_forward_noalloc": (ctypes.c_int, [_VP, _VP, _VP, _VP, ctypes.c_int, _VP, _VP, _I64,
+                                              _I64, _I64, _VP]),
     "bilogp_forward_ex": (ctypes.c_int, [_VP, _VP, _VP, _VP, ctypes.c_int, _VP, _VP, _I64, _I64,
                                          _I64, _VP, ctypes.c_size_t, _VP]),
     "bilogp_partials": (ctypes.c_int, [_VP, _VP, _VP, _VP, ctypes.c_int, _I64, _I64, _I64, _VP,
@@ -280,6 +283,27 @@ def bilogp_forward_ex(hidden: torch.Tensor, weight: torch.Tensor, target: torch.
                                    _bias_dtype(bias), _ptr(logp_out), _ptr(lse_out), N, H, V,
                                    _ptr(workspace), ws_bytes,
                                    _stream_handle(stream, hidden.device))
+    _check(st)
+
+
+def bilogp_noalloc_max_workspace_bytes() -> int:
+    return load_library().bilogp_noalloc_max_workspace_bytes()
+
+
+def bilogp_forward_noalloc(hidden: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
+                           bias: Optional[torch.Tensor], logp_out: torch.Tensor,
+                           lse_out: torch.Tensor, stream=None) -> None:
+    """``bilogp_forward_noalloc``: ``bilogp_forward_ex`` with the library's
+    per-GPU scratch array as the workspace; allocates nothing.  Calls that
+    overlap on one GPU race (they share the array)."""
+    N, H, V = _forward_args(hidden, weight, target, bias, (torch.bfloat16, torch.float32))
+    _outputs(N, logp_out, lse_out)
+    _same_device(hidden, weight, target, bias, logp_out, lse_out)
+    lib = load_library()
+    with torch.cuda.device(hidden.device):
+        st = lib.bilogp_forward_noalloc(_ptr(hidden), _ptr(weight), _ptr(target), _ptr(bias),
+                                        _bias_dtype(bias), _ptr(logp_out), _ptr(lse_out), N, H,
+                                        V, _stream_handle(stream, hidden.device))
     _check(st)
 
 

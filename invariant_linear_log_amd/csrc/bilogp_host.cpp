@@ -251,6 +251,9 @@ struct Call {
   // weight and bias then hold just those splits' vocabulary columns
   int split_begin = 0;
   int split_end = -1;
+  // the workspace is the library's own per-device scratch array (known to be
+  // device memory of the current device; not checked by pointer attributes)
+  bool ws_is_scratch = false;
 };
 
 // Full argument validation (fail closed) and the launch parameters.  Pure
@@ -343,7 +346,7 @@ bilogp_status validate(const Call& c, int parts, bilogp::ProjParams* out) {
   if (st != BILOGP_OK) return st;
   const void* ptrs[] = {proj ? c.hidden : nullptr, proj ? c.weight : nullptr, c.target,
                         proj ? c.bias : nullptr, merge ? c.logp : nullptr,
-                        merge ? c.lse : nullptr, c.ws};
+                        merge ? c.lse : nullptr, c.ws_is_scratch ? nullptr : c.ws};
   const char* names[] = {"hidden", "weight", "target", "bias", "logp_out", "lse_out", "workspace"};
   for (int i = 0; i < 7; ++i) {
     if (!ptrs[i]) continue;
@@ -527,6 +530,67 @@ bilogp_status bilogp_forward(const void* hidden, const void* weight, const int64
   if (e != hipSuccess)
     return fail(BILOGP_E_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(e));
   return BILOGP_OK;
+}
+
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Forward with no allocation at all: the workspace is a file-scope device
+// array of a fixed size, one copy per GPU, for callers that cannot allocate.
+// Its address is looked up once per device (hipGetSymbolAddress, with that
+// device current) and kept; host code never uses the array's name as an
+// address.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+bilogp_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0)
+    return fail(BILOGP_E_UNSUPPORTED, std::string("no usable HIP device: ") + hipGetErrorString(e));
+  if (dev >= kMaxDevices) return fail(BILOGP_E_UNSUPPORTED, "device index out of range");
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(BILOGP_E_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  }
+  *out = ptr;
+  return BILOGP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t bilogp_noalloc_max_workspace_bytes(void) { return kScratchBytes; }
+
+bilogp_status bilogp_forward_noalloc(const void* hidden, const void* weight,
+                                     const int64_t* target, const void* bias, int bias_dtype,
+                                     float* logp_out, float* lse_out, int64_t N, int64_t H,
+                                     int64_t V, void* stream) {
+  g_last_error.clear();
+  const size_t need = bilogp_workspace_bytes(N, V);
+  if (need != (size_t)-1 && need > kScratchBytes)
+    return fail(BILOGP_E_WORKSPACE, "the no-allocation forward holds at most " +
+                                        std::to_string(kScratchBytes) + " workspace bytes; N = " +
+                                        std::to_string(N) + ", V = " + std::to_string(V) +
+                                        " needs " + std::to_string(need));
+  Call c{hidden, weight, target, bias, bias_dtype, logp_out, lse_out, N, H, V, nullptr, 0};
+  if (need == (size_t)-1 || need == 0) return run(c, kProj | kMerge, stream);  // checks report it
+  void* ws = nullptr;
+  bilogp_status st = scratch_address(&ws);
+  if (st != BILOGP_OK) return st;
+  c.ws = ws;
+  c.ws_bytes = kScratchBytes;
+  c.ws_is_scratch = true;
+  return run(c, kProj | kMerge, stream);
 }
 
 }  // extern "C"
