@@ -34,14 +34,18 @@ METRIC = "tokens/s + TFLOP/s (MFMA %peak), linear-logp N=4096 H=4096 V=128256 bf
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0
 
-# HBM-side bytes per launch of proj_lse_kernel on the headline workload, from two
-# rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE), each scaled by what the same counter
-# reads for a plain 1 GiB device copy (x2.000 and x1.000).  Keyed by projection_digest()
-# of the code the counters were taken on (the kernel and its launch code, comments and
-# whitespace stripped): any change to that code reports null.
+# L2-miss (fabric) bytes per launch of proj_lse_kernel on the headline workload, from
+# two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE), each scaled by what the same
+# counter reads for a plain 1 GiB device copy (x2.000 and x1.000).  These are the bytes
+# the L2 exchanges with the memory side (the 256 MB Infinity Cache or HBM); no counter
+# available on gfx950 separates the HBM share.  Keyed by projection_digest() of the code
+# the counters were taken on (the kernel and its launch code, comments and whitespace
+# stripped): any change to that code reports null.
 MEASURED_TRAFFIC = {
-    ("headline", "02eb8814cc461444"): {"fetch_bytes": 6351805760, "write_bytes": 18801416},
 }
+TRAFFIC_KIND = ("L2-miss (fabric) bytes per launch: FETCH_SIZE + WRITE_SIZE, copy-calibrated; "
+                "served by the Infinity Cache or HBM - HBM bytes alone are not separable with "
+                "the counters available on gfx950")
 
 
 def parse():
@@ -62,6 +66,10 @@ def parse():
                     help="skip timing the deterministic backward")
     ap.add_argument("--no-invariance-cost", action="store_true",
                     help="skip timing the throughput split policy beside the invariant one")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing the other single-GPU configurations (medium, sweep, peaky)")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the board clock / power sample under sustained load")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of the workload the CPU oracle is timed on")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -109,12 +117,130 @@ def projection_digest():
     kernel source and the host code that picks its launch (row blocks, split
     runs)."""
     csrc = os.path.join(ROOT, "invariant_linear_log_amd", "csrc")
-    return code_digest(os.path.join(csrc, "proj_lse.hip"), os.path.join(csrc, "bilogp_host.cpp"))
+    return code_digest(os.path.join(csrc, "proj_fwd.hip"), os.path.join(csrc, "bilogp_host.cpp"))
 
 
 def measured_traffic(workload):
     rec = MEASURED_TRAFFIC.get((workload, projection_digest()))
     return None if rec is None else rec["fetch_bytes"] + rec["write_bytes"]
+
+
+def time_forward(h, t, w, b, steps, warmup, stream):
+    """Full forward steps (bilogp_partials + bilogp_merge, i.e. bilogp_forward_ex
+    with a caller workspace) on resident inputs; HIP events on the launch stream
+    around each kernel.  Returns per-step projection / merge / step times (ms)."""
+    import torch
+    import invariant_linear_log_amd as ila
+    N = h.shape[0]
+    V = w.shape[0]
+    logp = torch.empty(N, dtype=torch.float32, device=h.device)
+    lse = torch.empty(N, dtype=torch.float32, device=h.device)
+    ws = ila.workspace_for(N, V, h.device)
+    for _ in range(warmup):
+        ila.bilogp_partials(h, w, t, b, ws, stream=stream)
+        ila.bilogp_merge(t, ws, logp, lse, V, stream=stream)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in evs:
+        e[0].record(stream)
+        ila.bilogp_partials(h, w, t, b, ws, stream=stream)
+        e[1].record(stream)
+        ila.bilogp_merge(t, ws, logp, lse, V, stream=stream)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    proj = [e[0].elapsed_time(e[1]) for e in evs]
+    merge = [e[1].elapsed_time(e[2]) for e in evs]
+    step = [e[0].elapsed_time(e[2]) for e in evs]
+    ok = bool(torch.all(torch.isfinite(lse))) and bool(torch.all(logp <= 0))
+    return proj, merge, step, ok
+
+
+def config_legs(steps=10, warmup=3, names=("medium", "sweep", "peaky")):
+    """The other single-GPU configurations, each timed like the headline (full
+    forward step on resident inputs).  medium: N=512, H=1024, V=32000, fp32 bias;
+    sweep: N=4096, H=4096, V=151936, bf16 bias (the bias kernel, a 128-column
+    vocabulary tail); peaky: N=16384, H=8192, V=152064, hidden x8.  Targets are
+    the workloads' own (for peaky the uniform half; which tile holds a row's
+    target moves one 4-byte write, not the timing)."""
+    import torch
+    import synth
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    out = {}
+    for name in names:
+        inp = synth.make_inputs(name, device=dev)
+        wl = inp["workload"]
+        h = inp["hidden"].reshape(-1, wl.H).contiguous()
+        t = inp["target"].reshape(-1).contiguous()
+        w, b = inp["weight"], inp["bias"]
+        torch.cuda.synchronize()
+        proj, merge, step, ok = time_forward(h, t, w, b, steps, warmup, stream)
+        flops = 2.0 * wl.N * wl.H * wl.V
+        pm = sorted(proj)[len(proj) // 2]
+        sm = sorted(step)[len(step) // 2]
+        out[name] = {"N": wl.N, "H": wl.H, "V": wl.V, "bias": wl.bias,
+                     "step_ms": sm, "proj_lse_ms": pm,
+                     "merge_ms": sorted(merge)[len(merge) // 2],
+                     "tokens_per_s": wl.N / sm * 1e3, "tflops": flops / sm / 1e9,
+                     "proj_lse_tflops": flops / pm / 1e9,
+                     "frac": flops / pm / 1e9 / PEAK_BF16_TFLOPS, "outputs_sane": ok}
+        del inp, h, t, w, b
+        torch.cuda.empty_cache()
+    return out
+
+
+def clock_sample(run_step, seconds=3.0):
+    """Board clock and power while the headline step runs back to back for a few
+    seconds: `amd-smi metric` samples taken on a side thread (the timed region
+    itself is shorter than one sample).  The GFX clock is averaged over the
+    XCDs of each sample.  None if amd-smi is unavailable."""
+    import shutil
+    import subprocess
+    import threading
+    import torch
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+    samples = []
+    stop = threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                r = subprocess.run([exe, "metric", "-g", "0", "-p", "-c", "--json"],
+                                   capture_output=True, text=True, timeout=10)
+                d = json.loads(r.stdout)
+                g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+                clk = [v["clk"]["value"] for k, v in g["clock"].items()
+                       if k.startswith("gfx_") and isinstance(v, dict)]
+                samples.append((float(sum(clk)) / len(clk), float(g["power"]["socket_power"]["value"])))
+            except Exception:  # pragma: no cover - a missing field skips the sample
+                pass
+    th = threading.Thread(target=sampler)
+    t0 = time.perf_counter()
+    th.start()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(50):
+            run_step()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if len(samples) < 2:
+        return None
+    warm = samples[1:]                 # the first sample may predate the load
+    clks = [c for c, _ in warm]
+    pw = [p for _, p in warm]
+    cap = None
+    try:
+        import glob
+        for f in glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_cap"):
+            cap = int(open(f).read()) / 1e6
+            break
+    except Exception:  # pragma: no cover
+        pass
+    return {"gfx_mhz_mean": sum(clks) / len(clks), "gfx_mhz_min": min(clks),
+            "gfx_mhz_max": max(clks), "power_w_mean": sum(pw) / len(pw), "power_cap_w": cap,
+            "samples": len(warm), "seconds": seconds,
+            "source": "amd-smi metric -p -c during back-to-back headline steps"}
 
 
 def invariance_cost(h, t, w, b, steps=10, warmup=3):
@@ -468,8 +594,13 @@ def main():
                      "algorithmic_hbm_gbps": algorithmic_bytes(N, H, V, S, bias_bytes)
                      / avg_proj_s / 1e9,
                      "traffic": measured_traffic(wl.name),
-                     "traffic_unit": "bytes per launch"},
+                     "traffic_unit": "bytes per launch",
+                     "traffic_kind": TRAFFIC_KIND},
     }
+    if not args.no_clock:
+        out["clock"] = clock_sample(step)
+    if not args.no_configs:
+        out["configs"] = config_legs()
     if not args.no_invariance_cost:
         out["invariance_cost"] = invariance_cost(h, t, w, b)
     if not args.no_backward:

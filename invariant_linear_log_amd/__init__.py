@@ -57,6 +57,7 @@ from ._binding import (  # noqa: F401
     bilogp_forward_mode,
     bilogp_forward_noalloc,
     bilogp_last_error,
+    bilogp_launch_plan,
     bilogp_max_splits,
     bilogp_merge,
     bilogp_noalloc_max_workspace_bytes,
@@ -158,7 +159,8 @@ def forward(hidden: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
         bias_1d = None if bias is None else bias.contiguous()
         N = hidden_2d.shape[0]
         if check_targets and N > 0:
-            lo, hi = int(target_1d.min()), int(target_1d.max())
+            # one device-to-host read for both bounds
+            lo, hi = torch.stack(torch.aminmax(target_1d)).tolist()
             if lo < 0 or hi >= V:
                 raise ValueError(f"target outside [0, {V}): min {lo}, max {hi}")
         logp = torch.empty(N, dtype=torch.float32, device=dev)

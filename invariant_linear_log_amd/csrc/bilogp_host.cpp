@@ -453,6 +453,22 @@ bilogp_status run(const Call& c, int parts, void* stream) {
 
 extern "C" {
 
+int bilogp_launch_plan(int64_t N, int64_t V, int mode, int cu_count, int* rows_per_block,
+                       int* splits_per_workgroup, int64_t* workgroups) {
+  if (N < 1 || N > kMaxN || V <= 0 || V > kMaxV || cu_count < 1 || cu_count > kMaxCuCount)
+    return -1;
+  const int S = bilogp_num_vocab_splits_mode(N, V, mode, cu_count);
+  const int vps = bilogp_vtiles_per_split_mode(N, V, mode, cu_count);
+  if (S == 0 || vps == 0) return -1;
+  const int32_t rows = row_block_rows(N, S, cu_count);
+  const int64_t R = (N + rows - 1) / rows;
+  const int32_t spg = splits_per_run(R, S, vps, cu_count);
+  if (rows_per_block) *rows_per_block = rows;
+  if (splits_per_workgroup) *splits_per_workgroup = spg;
+  if (workgroups) *workgroups = R * ((S + spg - 1) / spg);
+  return 0;
+}
+
 bilogp_status bilogp_forward_ex(const void* hidden, const void* weight, const int64_t* target,
                                 const void* bias, int bias_dtype, float* logp_out,
                                 float* lse_out, int64_t N, int64_t H, int64_t V,

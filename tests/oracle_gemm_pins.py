@@ -95,7 +95,7 @@ def pin_single_row_outer_product(orc):
 
 def pin_symmetry_and_abs(orc):
     """fwd(A, B) = fwd(B, A)^T; |terms| sums bound |results| and equal them for
-    non-negative operands."""
+    non-negative operands (forward, dA and dB)."""
     a, b = _bf16((6, 16), 70), _bf16((11, 16), 71)
     _assert(np.array_equal(orc.det_gemm_fwd(a, b), orc.det_gemm_fwd(b, a).T), "symmetry")
     c = orc.det_gemm_fwd(a, b)
@@ -108,6 +108,14 @@ def pin_symmetry_and_abs(orc):
             "abs da")
     _assert(np.all(np.abs(orc.det_gemm_db(a, dc)) <= orc.abs_product("db", a, dc) * (1 + 1e-15)),
             "abs db")
+    # with non-negative operands every term is its own absolute value, so the
+    # sums of |terms| equal the products exactly (an over-estimate, which
+    # would loosen the GPU tolerances built on them, fails here)
+    pdc = dc.abs()
+    _assert(np.allclose(orc.det_gemm_da(pdc, pb), orc.abs_product("da", pdc, pb), rtol=1e-15,
+                        atol=0), "abs da equal")
+    _assert(np.allclose(orc.det_gemm_db(pa, pdc), orc.abs_product("db", pa, pdc), rtol=1e-15,
+                        atol=0), "abs db equal")
 
 
 ALL_PINS = [pin_brute_force, pin_worked_example, pin_adjoint_identity,

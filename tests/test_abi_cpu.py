@@ -544,3 +544,27 @@ def test_partials_range_empty_batch_and_columns():
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU path")
 def test_partials_range_no_device_is_unsupported():
     assert _call_range(0, 8) == B.BILOGP_E_UNSUPPORTED
+
+
+def test_launch_plan_follows_the_compute_units_only_in_scheduling():
+    inv, tp = B.BILOGP_SPLITS_INVARIANT, B.BILOGP_SPLITS_THROUGHPUT
+    V = 151936                                   # 594 tiles, 198 splits of 3
+    cus = (1, 8, 32, 80, 128, 256, 304, 1024, 4096, 65536)
+    for n in (1, 7, 300, 4096):
+        plans = {cu: ila.bilogp_launch_plan(n, V, inv, cu) for cu in cus}
+        for cu, (rows, spg, wgs) in plans.items():
+            assert rows in (128, 256) and spg >= 1
+            assert wgs == -(-n // rows) * -(-198 // spg)
+        # few compute units: 256-token blocks; enough of them: 128-token blocks
+        assert plans[1][0] == 256 and plans[65536][0] == 128
+        assert len(set(plans.values())) >= 2
+    # at the headline V (2 tiles per split) the splits per workgroup follow the count too
+    hp = {cu: ila.bilogp_launch_plan(4096, 128256, inv, cu) for cu in (1, 100, 256, 1000)}
+    assert len({spg for _, spg, _ in hp.values()}) >= 2, hp
+    assert ila.bilogp_launch_plan(4096, 128256, inv, 256) == (256, 2, 16 * 126)
+    assert ila.bilogp_launch_plan(0, 1000, inv, 256) is None
+    assert ila.bilogp_launch_plan(8, 0, inv, 256) is None
+    assert ila.bilogp_launch_plan(8, 1000, inv, 0) is None
+    assert ila.bilogp_launch_plan(8, 1000, 7, 256) is None
+    # the throughput mode's split count follows the same count
+    assert ila.bilogp_launch_plan(8, 128256, tp, 256) is not None

@@ -154,3 +154,35 @@ def test_odd_row_block_counts_keep_the_bits(rows):
     assert torch.equal(lp, full_lp[:rows]) and torch.equal(ls, full_ls[:rows])
     assert torch.equal(torch.cat(lps), full_lp[:rows])
     assert torch.equal(torch.cat(lss), full_ls[:rows])
+
+
+CU_COUNTS = [1, 8, 32, 80, 128, 256, 304, 1024, 4096, 65536]
+
+
+@pytest.mark.parametrize("n", [1, 7, 300, 4096])
+def test_compute_unit_count_never_changes_bits(n):
+    """The bits never depend on the number of compute units (RL-Kernel PR
+    #337, description, "Why this happens": the SM count is the input that
+    made the scheduler it replaces change a row's reduction).  The launch is
+    scheduled for each count in turn - row-block height and splits per
+    workgroup differ (checked on the host plan) - on the sweep workload (bf16
+    bias, 128-column vocabulary tail), and every result equals
+    bilogp_forward_ex's bit for bit."""
+    inp, full_lp, full_ls = sweep_inputs()
+    h, t = flat(inp)
+    h, t = h[:n].contiguous(), t[:n].contiguous()
+    w, b = inp["weight"], inp["bias"]
+    V = w.shape[0]
+    ref_lp, ref_ls = run_ex(h, w, t, b)
+    plans = set()
+    for cu in CU_COUNTS:
+        plans.add(ila.bilogp_launch_plan(n, V, ila.BILOGP_SPLITS_INVARIANT, cu))
+        say(f"sweep n={n} cu_count={cu}")
+        lp = torch.empty(n, device=DEV)
+        ls = torch.empty(n, device=DEV)
+        ws = ila.workspace_for(n, V, DEV)
+        ila.bilogp_forward_mode(h, w, t, b, lp, ls, ila.BILOGP_SPLITS_INVARIANT, cu, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(lp, ref_lp) and torch.equal(ls, ref_ls), f"bits differ at cu={cu}"
+        assert torch.equal(lp, full_lp[:n]) and torch.equal(ls, full_ls[:n])
+    assert len(plans) >= 2, f"the counts gave one plan only: {plans}"

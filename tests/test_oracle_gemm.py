@@ -28,6 +28,9 @@ MUTATIONS = {
     "db_sign": ("return G.T @ A", "return -(G.T @ A)"),
     "db_drops_first_row": ("return G.T @ A", "return G[1:].T @ A[1:]"),
     "brute_drops_last_term": ("for k in range(K)", "for k in range(K - 1)"),
+    # over-estimated error scales (they would only loosen the GPU tolerances)
+    "abs_da_doubled": ("        return X @ Y\n", "        return 2 * (X @ Y)\n"),
+    "abs_db_plus_one": ("        return Y.T @ X\n", "        return Y.T @ X + 1\n"),
 }
 
 
