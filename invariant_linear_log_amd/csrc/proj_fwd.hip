@@ -144,6 +144,9 @@ __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
   __shared__ __attribute__((aligned(1024))) uint8_t slot1[kBuf];
   __shared__ __attribute__((aligned(1024))) uint8_t slot2[kSlots == 3 ? kBuf : 16];
   __shared__ float2 red[kBlockRows];
+  // each token's target (-1 outside [0, V)), read once per tile by the
+  // epilogue: kept in LDS rather than in registers through the stage loop
+  __shared__ int tgt_lds[kBlockRows];
   // bias of the current and the next vocabulary tile (bias kernels only)
   __shared__ __attribute__((aligned(16))) float bias_lds[2][kVtileCols];
 
@@ -232,13 +235,10 @@ __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
     b_off[uu] = kTileBytes + ((wt * kWaveTok + lr) * kChunks + c) * 16;
   }
 
-  // ---- targets of this lane's token columns (kTj of them) -------------------
-  int tgt[kTj];          // the target, or -1 when outside [0, V) (V <= 2^30)
-#pragma unroll
-  for (int tj = 0; tj < kTj; ++tj) {
-    const int j = wt * kWaveTok + tj * 16 + lr;
-    const int64_t t = (j < rows_here) ? p.target[m0 + j] : (int64_t)-1;
-    tgt[tj] = (t >= 0 && t < p.V) ? (int)t : -1;
+  // ---- targets of the block's tokens (visible after the prologue barrier) --
+  if (tid < kRows) {
+    const int64_t t = (tid < rows_here) ? p.target[m0 + tid] : (int64_t)-1;
+    tgt_lds[tid] = (t >= 0 && t < p.V) ? (int)t : -1;     // V <= 2^30
   }
 
   // Direct-to-LDS loads of stage g into buffer SC, one instruction at a
@@ -318,21 +318,23 @@ __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
     // load); with three, where a barrier leaves the newest six loads in
     // flight, the first one after six more loads - one or two stages on, long
     // before the epilogue.  Nothing bias-related runs in the stage loop.
-    const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const float*)p.bias + (int64_t)vt_begin * kVtileCols), (short)0,
-        kHasBias ? nvt * kVtileCols * 4 : 0, kRsrcWord3);     // unused without bias
+    // The descriptor is built per load from the kernel argument, so nothing
+    // bias-related stays live in registers through the stage loop.
     auto load_bias = [&](int v) {
       if constexpr (kHasBias) {
-        if (wave == 0 && v < nvt)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_b, (lds_void*)&bias_lds[v & 1][0], 16,
-                                                   (uint32_t)v * 1024u + (uint32_t)lane * 16u, 0, 0,
-                                                   0);
+        if (wave == 0 && v < nvt) {
+          const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+              (void*)((const float*)p.bias + (int64_t)(vt_begin + v) * kVtileCols), (short)0,
+              kVtileCols * 4, kRsrcWord3);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)&bias_lds[v & 1][0], 16,
+                                                   (uint32_t)lane * 16u, 0, 0, 0);
+        }
       }
     };
     auto init_acc = [&]() {
-  #pragma unroll
+#pragma unroll
       for (int vi = 0; vi < 8; ++vi)
-  #pragma unroll
+#pragma unroll
         for (int tj = 0; tj < kTj; ++tj) acc[vi][tj] = floatx4{};
     };
 
@@ -361,7 +363,7 @@ __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
                      auto is_h, auto nloads, auto last, auto sync) {
       constexpr bool kLast = decltype(last)::value;
       constexpr int kNl = decltype(nloads)::value;
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < kM; ++i) {
         const int vi = i / kTj, tj = i % kTj;
         acc[vi][tj] =
@@ -386,7 +388,7 @@ __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
             const int q = i - kBarAt - 1;
             if (tj == 0 && vi + 3 >= 8) ar[(vi + 3) & 3] = rd_a(nst, nu, vi + 3 - 8);
             if (q < kTj) bn[q] = rd_b(nst, nu, q);
-  #pragma unroll
+#pragma unroll
             for (int j = 0; j < kLoadsW; ++j)
               if (q == j * kPost / kLoadsW) ld(lc, j, std::false_type{});
           }
@@ -437,7 +439,7 @@ __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
     };
 
     float m_run[kTj], s_run[kTj];
-  #pragma unroll
+#pragma unroll
     for (int tj = 0; tj < kTj; ++tj) {
       m_run[tj] = -INFINITY;
       s_run[tj] = 0.f;
@@ -451,10 +453,10 @@ __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
     // `red` is free again by the next flush, at least one stage barrier later.
     auto flush = [&](int split) {
       float mm[kTj], ss[kTj];
-  #pragma unroll
+#pragma unroll
       for (int tj = 0; tj < kTj; ++tj) {
         float m = m_run[tj], s = s_run[tj];
-  #pragma unroll
+#pragma unroll
         for (int d = 16; d <= 32; d <<= 1) {
           const float om = __shfl_xor(m, d);
           const float os = __shfl_xor(s, d);
@@ -467,13 +469,13 @@ __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
         ss[tj] = s;
       }
       if (wv == 1 && lg == 0) {
-  #pragma unroll
+#pragma unroll
         for (int tj = 0; tj < kTj; ++tj)
           red[wt * kWaveTok + tj * 16 + lr] = make_float2(mm[tj], ss[tj]);
       }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       if (wv == 0 && lg == 0) {
-  #pragma unroll
+#pragma unroll
         for (int tj = 0; tj < kTj; ++tj) {
           const int j = wt * kWaveTok + tj * 16 + lr;
           const float2 hi = red[j];
@@ -482,7 +484,7 @@ __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
           if (j < rows_here) p.part[(m0 + j) * p.S + split] = make_float2(m, s);
         }
       }
-  #pragma unroll
+#pragma unroll
       for (int tj = 0; tj < kTj; ++tj) {
         m_run[tj] = -INFINITY;
         s_run[tj] = 0.f;
@@ -494,17 +496,17 @@ __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
     // and the W slice of stage 2.
     {
       const LoadCtx w0 = ctx_w(0, Slot<0>{}), h0 = ctx_h(0, Slot<0>{}), w1 = ctx_w(1, Slot<1>{});
-  #pragma unroll
+#pragma unroll
       for (int j = 0; j < kLoadsW; ++j) ld(w0, j, std::false_type{});
-  #pragma unroll
+#pragma unroll
       for (int j = 0; j < kLoadsH; ++j) ld(h0, j, std::true_type{});
-  #pragma unroll
+#pragma unroll
       for (int j = 0; j < kLoadsW; ++j) ld(w1, j, std::false_type{});
       if constexpr (kSlots == 3) {
         const LoadCtx h1 = ctx_h(1, Slot<1>{}), w2 = ctx_w(2, Slot<2>{});
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < kLoadsH; ++j) ld(h1, j, std::true_type{});
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < kLoadsW; ++j) ld(w2, j, std::false_type{});
       }
       load_bias(0);
@@ -512,9 +514,9 @@ __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
     wait_vmcnt<0>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     init_acc();
-  #pragma unroll
+#pragma unroll
     for (int vi = 0; vi < 3; ++vi) ar[vi] = rd_a(slot0, 0, vi);
-  #pragma unroll
+#pragma unroll
     for (int tj = 0; tj < kTj; ++tj) bA[tj] = rd_b(slot0, 0, tj);
 
     // G is a multiple of kSlots: stage g lives in buffer g % kSlots.
@@ -538,42 +540,46 @@ __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
         // z = (the K accumulation) + bias: one fp32 add per logit
         __builtin_amdgcn_sched_barrier(0);
         const float* bt = &bias_lds[v & 1][wv * 128 + 4 * lg];
-  #pragma unroll
+#pragma unroll
         for (int vi = 0; vi < 8; ++vi) {
           const floatx4 bb = *(const floatx4*)(bt + vi * 16);
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 4; ++e)
-  #pragma unroll
+#pragma unroll
             for (int tj = 0; tj < kTj; ++tj) acc[vi][tj][e] += bb[e];
+          // in place: without these the compiler gives the sums new registers
+          // and spills values that live through the stage loop
+#pragma unroll
+          for (int tj = 0; tj < kTj; ++tj) asm volatile("" : "+v"(acc[vi][tj]));
           __builtin_amdgcn_sched_barrier(0);        // a few bias values live at a time
         }
         load_bias(v + 1);          // lands during the next tile's first stage
       }
       if (vbase + kVtileCols > p.V) {                // vocabulary tail: mask columns >= V
-  #pragma unroll
+#pragma unroll
         for (int vi = 0; vi < 8; ++vi)
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int col = vw + vi * 16 + 4 * lg + e;
             if (col >= p.V) {
-  #pragma unroll
+#pragma unroll
               for (int tj = 0; tj < kTj; ++tj) acc[vi][tj][e] = -INFINITY;
             }
           }
       }
 
-  #pragma unroll
+#pragma unroll
       for (int tj = 0; tj < kTj; ++tj) {
         // target capture: exactly one (tile, lane, register) in the grid holds it
-        const int rel = tgt[tj] - vw;
+        const int rel = tgt_lds[wt * kWaveTok + tj * 16 + lr] - vw;
         const bool hit = rel >= 0 && rel < 128 && ((rel >> 2) & 3) == lg;
         if (__any(hit)) {
           const int vi_t = rel >> 4;
           const int e_t = rel & 3;
           float val = 0.f;
-  #pragma unroll
+#pragma unroll
           for (int vi = 0; vi < 8; ++vi)
-  #pragma unroll
+#pragma unroll
             for (int e = 0; e < 4; ++e)
               if (vi == vi_t && e == e_t) val = acc[vi][tj][e];
           if (hit) p.tlogit[m0 + wt * kWaveTok + tj * 16 + lr] = val;
@@ -581,16 +587,16 @@ __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
 
         // online softmax over this lane's 32 values of the tile
         float mx = acc[0][tj][0];
-  #pragma unroll
+#pragma unroll
         for (int vi = 0; vi < 8; ++vi)
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 4; ++e) mx = fmaxf(mx, acc[vi][tj][e]);
         const float m_new = fmaxf(m_run[tj], mx);
         const float mu = (m_new == -INFINITY) ? 0.f : m_new;
         float ps[4] = {0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
+#pragma unroll
         for (int vi = 0; vi < 8; ++vi)
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 4; ++e) ps[e] += exp2_hw((acc[vi][tj][e] - mu) * kLog2e);
         const float tile_sum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
         s_run[tj] = s_run[tj] * exp2_hw((m_run[tj] - mu) * kLog2e) + tile_sum;
