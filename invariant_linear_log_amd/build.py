@@ -22,7 +22,7 @@ LIB_NAME = "libbilogp.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["bilogp_host.cpp", "proj_fwd.hip", "proj_lse.hip", "merge.hip", "det_gemm.hip"]
+SOURCES = ["bilogp_host.cpp", "proj_fwd.hip", "aux_kernels.hip", "merge.hip", "det_gemm.hip"]
 
 # Packed fp32 VALU forms are kept out of all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -126,10 +126,21 @@ __device__ __forceinline__ void merge_state(float m_lo, float s_lo, float m_hi, 
 template <int I>
 using Slot = std::integral_constant<int, I>;
 
-// The forward body.  kTj token blocks of 16 per wave: 4 (256-token row
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// The kernel body.  kTj token blocks of 16 per wave: 4 (256-token row
 // blocks) or 2 (128-token row blocks, for batches too small to give every
-// compute unit a 256-token block); kSlots LDS buffers.
-template <bool kHasBias, int kTj, int kSlots>
+// compute unit a 256-token block); kSlots LDS buffers.  With kGrad it is the
+// softmax-gradient pass of the backward: the same tiles and the same
+// accumulation (z has the forward's bits), and a tile epilogue that writes
+// dZ = p (g_lse - g_logp) + g_logp [v == target], p = exp(z - lse), instead
+// of reducing it.
+template <bool kHasBias, bool kGrad, int kTj, int kSlots>
 __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
   static_assert(kTj == 4 || kTj == 2, "two or four 16-token blocks per wave");
   static_assert(kSlots == 2 || (kSlots == 3 && kTj == 2), "three buffers fit 128-token blocks");
@@ -147,6 +158,8 @@ __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
   // each token's target (-1 outside [0, V)), read once per tile by the
   // epilogue: kept in LDS rather than in registers through the stage loop
   __shared__ int tgt_lds[kBlockRows];
+  // backward: per token the forward's lse, g_lse - g_logp and g_logp
+  __shared__ float grad_lds[3][kGrad ? kBlockRows : 1];
   // bias of the current and the next vocabulary tile (bias kernels only)
   __shared__ __attribute__((aligned(16))) float bias_lds[2][kVtileCols];
 
@@ -239,6 +252,13 @@ __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
   if (tid < kRows) {
     const int64_t t = (tid < rows_here) ? p.target[m0 + tid] : (int64_t)-1;
     tgt_lds[tid] = (t >= 0 && t < p.V) ? (int)t : -1;     // V <= 2^30
+    if constexpr (kGrad) {
+      const bool live = tid < rows_here;
+      const float gl = live ? p.g_logp[m0 + tid] : 0.f;
+      grad_lds[0][tid] = live ? p.lse[m0 + tid] : 0.f;
+      grad_lds[1][tid] = live ? p.g_lse[m0 + tid] - gl : 0.f;
+      grad_lds[2][tid] = gl;
+    }
   }
 
   // Direct-to-LDS loads of stage g into buffer SC, one instruction at a
@@ -555,6 +575,55 @@ __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
         }
         load_bias(v + 1);          // lands during the next tile's first stage
       }
+      if constexpr (kGrad) {
+        // dZ^T[col][row] = p (g_lse - g_logp) + g_logp [col == target], p =
+        // exp(z - lse), rounded to bf16.  One store per (vi, e, tj): each
+        // lane group writes 16 consecutive tokens of one vocabulary row, and
+        // the kTj stores of an (vi, e) complete the wave's 64 tokens (a whole
+        // 128-byte line) of each of its four rows back to back.  The buffer
+        // covers the tile's columns below V, so stores past V are dropped.
+        const int vrows = min(kVtileCols, p.V - vbase);
+        const __amdgpu_buffer_rsrc_t rs_dz = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(p.dzt + (int64_t)vbase * p.ldz), (short)0, vrows * (int)p.ldz * 2,
+            kRsrcWord3);
+        uint32_t vo[kTj];
+        bool live[kTj];
+        int trel[kTj];
+        float lse_r[kTj], coef[kTj], gtg[kTj];
+#pragma unroll
+        for (int tj = 0; tj < kTj; ++tj) {
+          const int jr = wt * kWaveTok + tj * 16 + lr;
+          live[tj] = jr < rows_here;
+          vo[tj] = ((uint32_t)(wv * 128 + 4 * lg) * (uint32_t)p.ldz + (uint32_t)(m0 + jr)) * 2u;
+          // opaque per tile: the store addresses are formed here, not hoisted
+          // out of the stage loop into registers that would then spill
+          asm volatile("" : "+v"(vo[tj]));
+          trel[tj] = tgt_lds[jr] - vw - 4 * lg;
+          lse_r[tj] = grad_lds[0][jr];
+          coef[tj] = grad_lds[1][jr];
+          gtg[tj] = grad_lds[2][jr];
+        }
+        uint32_t ld2 = (uint32_t)p.ldz * 2u;
+        asm volatile("" : "+s"(ld2));
+#pragma unroll
+        for (int vi = 0; vi < 8; ++vi) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int k = vi * 16 + e;                // column - vw - 4 lg
+#pragma unroll
+            for (int tj = 0; tj < kTj; ++tj) {
+              float dz = exp2_hw((acc[vi][tj][e] - lse_r[tj]) * kLog2e) * coef[tj];
+              if (trel[tj] == k) dz += gtg[tj];
+              if (live[tj])
+                __builtin_amdgcn_raw_buffer_store_b16(bf16_rne(dz), rs_dz,
+                                                      vo[tj] + (uint32_t)k * ld2, 0, 0);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        init_acc();
+        continue;
+      }
       if (vbase + kVtileCols > p.V) {                // vocabulary tail: mask columns >= V
 #pragma unroll
         for (int vi = 0; vi < 8; ++vi)
@@ -619,21 +688,43 @@ __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
 }
 
 __global__ __launch_bounds__(kThreads, 1) void proj_lse_kernel(const ProjParams p) {
-  proj_fwd_body<false, 4, 2>(p);
+  proj_fwd_body<false, false, 4, 2>(p);
 }
 __global__ __launch_bounds__(kThreads, 1) void proj_lse_bias_kernel(const ProjParams p) {
-  proj_fwd_body<true, 4, 2>(p);
+  proj_fwd_body<true, false, 4, 2>(p);
+}
+__global__ __launch_bounds__(kThreads, 1) void softmax_grad_kernel(const ProjParams p) {
+  proj_fwd_body<false, true, 4, 2>(p);
+}
+__global__ __launch_bounds__(kThreads, 1) void softmax_grad_bias_kernel(const ProjParams p) {
+  proj_fwd_body<true, true, 4, 2>(p);
 }
 // 128-token row blocks: twice the workgroups for batches that 256-token
 // blocks cannot spread over every compute unit; the same bits
 __global__ __launch_bounds__(kThreads, 1) void proj_lse_r128_kernel(const ProjParams p) {
-  proj_fwd_body<false, 2, 3>(p);
+  proj_fwd_body<false, false, 2, 3>(p);
 }
 __global__ __launch_bounds__(kThreads, 1) void proj_lse_bias_r128_kernel(const ProjParams p) {
-  proj_fwd_body<true, 2, 3>(p);
+  proj_fwd_body<true, false, 2, 3>(p);
+}
+__global__ __launch_bounds__(kThreads, 1) void softmax_grad_r128_kernel(const ProjParams p) {
+  proj_fwd_body<false, true, 2, 3>(p);
+}
+__global__ __launch_bounds__(kThreads, 1) void softmax_grad_bias_r128_kernel(const ProjParams p) {
+  proj_fwd_body<true, true, 2, 3>(p);
 }
 
 }  // namespace
+
+hipError_t launch_softmax_grad(const ProjParams& p, hipStream_t stream) {
+  const int64_t blocks = (int64_t)p.R * p.S_grid;
+  if (blocks <= 0) return hipSuccess;
+  const bool bias = p.bias_kind != kBiasNone;
+  auto k = p.rows == 128 ? (bias ? softmax_grad_bias_r128_kernel : softmax_grad_r128_kernel)
+                         : (bias ? softmax_grad_bias_kernel : softmax_grad_kernel);
+  hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_proj_lse(const ProjParams& p, hipStream_t stream) {
   const int64_t blocks = (int64_t)p.R * p.S_grid;
