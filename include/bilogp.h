@@ -61,12 +61,15 @@ extern "C" {
 #define BILOGP_ABI_VERSION 2
 
 /* Version of the bit contract: for given inputs of one row (its hidden row
- * and target, W, bias, H, V), which fp32 bits logp and lse take.  The page
- * fixes no bits (several fp32 results are equally correct, PR #337
- * description, "Why this happens"); what this library promises is that the
- * bits of one version never depend on N, the row's position, the other rows,
- * the stream or the compute units.  A change to anything that orders the
- * arithmetic changes the version:
+ * and target, W, bias, H, V), which fp32 bits logp and lse take, and for the
+ * deterministic GEMM and backward, which bits their outputs take for given
+ * operands.  The page fixes no bits (several fp32 results are equally
+ * correct, PR #337 description, "Why this happens"); what this library
+ * promises is that the bits of one version never depend on N, the row's
+ * position, the other rows, the stream or the compute units (for the
+ * weight gradients: on anything but the rows themselves, reduced in
+ * ascending order).  A change to anything that orders the arithmetic
+ * changes the version:
  *   1  tiles of 256 columns, at most 64 splits; merge tree whose lanes
  *      pre-summed strided splits
  *   2  tiles of 256 columns, at most 256 splits; merge tree whose lanes
@@ -79,8 +82,12 @@ extern "C" {
  *      v_mfma_f32_16x16x32_bf16, and per token each lane sums its 32 values
  *      of a tile (8 blocks of 4 vocabulary rows) in a fixed register order,
  *      then the four lane groups (pairs 16 lanes apart, then 32 apart) and
- *      the two vocabulary-half waves are merged in fixed operand order */
-#define BILOGP_BIT_CONTRACT_VERSION 3
+ *      the two vocabulary-half waves are merged in fixed operand order
+ *   4  forward as 3; the deterministic GEMM (bilogp_det_gemm_*) and the
+ *      backward's two products reduce in ascending 32-wide steps of
+ *      v_mfma_f32_16x16x32_bf16 (before: 16-wide steps of
+ *      v_mfma_f32_32x32x16_bf16) */
+#define BILOGP_BIT_CONTRACT_VERSION 4
 
 typedef enum bilogp_status {
   BILOGP_OK = 0,

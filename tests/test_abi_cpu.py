@@ -40,9 +40,10 @@ def test_constants_and_version():
     # most 256 splits, the merge tree over consecutive per-lane split blocks
     # (contract 1 had at most 64 splits and lane-strided pre-sums).  Bit
     # contract 3: K in 32-wide steps of the 16 x 16 x 32 bf16 MFMA, per-token
-    # sums over (lane group, register) of that tile layout.
+    # sums over (lane group, register) of that tile layout.  Bit contract 4:
+    # the deterministic GEMM and the backward's products on that MFMA too.
     assert ila.bilogp_abi_version() == 2
-    assert ila.bilogp_bit_contract_version() == 3
+    assert ila.bilogp_bit_contract_version() == 4
     assert ila.bilogp_vtile_cols() == 256
     assert ila.bilogp_max_splits() == 256
     for s in range(5):
