@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define BILOGP_ABI_VERSION 2
+#define BILOGP_ABI_VERSION 3
 
 /* Version of the bit contract: for given inputs of one row (its hidden row
  * and target, W, bias, H, V), which fp32 bits logp and lse take, and for the
@@ -171,15 +171,16 @@ int bilogp_num_vocab_splits_mode(int64_t N, int64_t V, int mode, int cu_count);
  * the mode's split count).  (size_t)-1 on invalid arguments, 0 for N == 0. */
 size_t bilogp_workspace_bytes_mode(int64_t N, int64_t V, int mode, int cu_count);
 
-/* Launch plan of the projection for N rows under `mode`, scheduled for
- * cu_count compute units (what bilogp_forward_mode does with the same
- * arguments): tokens per row block (256, or 128 when 256-token blocks would
- * leave units idle), consecutive splits per workgroup, and the workgroup
- * count.  Scheduling only - in the invariant mode no output bit depends on
- * it.  Host-side, no device needed.  Returns 0, or -1 for N < 1, V or
- * cu_count out of range, or an unknown mode (outputs untouched). */
-int bilogp_launch_plan(int64_t N, int64_t V, int mode, int cu_count, int* rows_per_block,
-                       int* splits_per_workgroup, int64_t* workgroups);
+/* Launch plan of the projection for N rows of H features under `mode`,
+ * scheduled for cu_count compute units (what bilogp_forward_mode does with
+ * the same arguments): tokens per row block (256, or 128 when 256-token
+ * blocks would leave units idle and the 128-token plan has the shorter
+ * critical path), consecutive splits per workgroup, and the workgroup count.
+ * Scheduling only - in the invariant mode no output bit depends on it.
+ * Host-side, no device needed.  Returns 0, or -1 for N < 1, H, V or cu_count
+ * out of range, or an unknown mode (outputs untouched).  (ABI 3 added H.) */
+int bilogp_launch_plan(int64_t N, int64_t H, int64_t V, int mode, int cu_count,
+                       int* rows_per_block, int* splits_per_workgroup, int64_t* workgroups);
 
 /* Fused forward with an optional fp32 bias and a library-managed workspace
  * (stream-ordered hipMallocAsync / hipFreeAsync on `stream`).

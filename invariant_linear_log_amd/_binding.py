@@ -52,7 +52,7 @@ SIGNATURES = {
     "bilogp_vtiles_per_split_mode": (ctypes.c_int, [_I64, _I64, ctypes.c_int, ctypes.c_int]),
     "bilogp_num_vocab_splits_mode": (ctypes.c_int, [_I64, _I64, ctypes.c_int, ctypes.c_int]),
     "bilogp_workspace_bytes_mode": (ctypes.c_size_t, [_I64, _I64, ctypes.c_int, ctypes.c_int]),
-    "bilogp_launch_plan": (ctypes.c_int, [_I64, _I64, ctypes.c_int, ctypes.c_int,
+    "bilogp_launch_plan": (ctypes.c_int, [_I64, _I64, _I64, ctypes.c_int, ctypes.c_int,
                                           ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
                                           ctypes.POINTER(ctypes.c_int64)]),
     "bilogp_forward_mode": (ctypes.c_int, [_VP, _VP, _VP, _VP, ctypes.c_int, _VP, _VP, _I64, _I64,
@@ -232,11 +232,11 @@ def bilogp_workspace_bytes_mode(N: int, V: int, mode: int, cu_count: int) -> int
     return load_library().bilogp_workspace_bytes_mode(N, V, mode, cu_count)
 
 
-def bilogp_launch_plan(N: int, V: int, mode: int, cu_count: int):
+def bilogp_launch_plan(N: int, H: int, V: int, mode: int, cu_count: int):
     """(tokens per row block, splits per workgroup, workgroups) of the
     projection launch, or None for invalid arguments."""
     rows, spg, wgs = ctypes.c_int(), ctypes.c_int(), ctypes.c_int64()
-    st = load_library().bilogp_launch_plan(N, V, mode, cu_count, ctypes.byref(rows),
+    st = load_library().bilogp_launch_plan(N, H, V, mode, cu_count, ctypes.byref(rows),
                                            ctypes.byref(spg), ctypes.byref(wgs))
     return None if st != 0 else (rows.value, spg.value, wgs.value)
 

@@ -89,15 +89,6 @@ bilogp_status check_device(int* dev_out) {
   return BILOGP_OK;
 }
 
-// Row-block height of a projection launch: 256 tokens, or 128 when 256-token
-// blocks give fewer workgroups than `cu` compute units.  A row's arithmetic
-// is the same in either (row blocking never changes bits), so the choice may
-// follow N and the device.
-int32_t row_block_rows(int64_t N, int64_t splits, int cu) {
-  const int64_t r256 = (N + 255) / 256;
-  return (cu > 0 && r256 * splits < cu) ? 128 : 256;
-}
-
 // Consecutive splits per projection workgroup.  It only schedules the work:
 // each split's partial is written by the same arithmetic however the splits
 // are grouped.  Candidates are 1 .. about kTilesPerRun tiles' worth of
@@ -126,6 +117,37 @@ int32_t splits_per_run(int64_t R, int nsplits, int vps, int cu) {
     }
   }
   return best;
+}
+
+// K stages a compute unit runs for R row blocks: whole rounds of one
+// workgroup per unit, each workgroup a run of splits of vps tiles of kt
+// stages (the run length as splits_per_run chooses it).
+int64_t plan_stages(int64_t R, int nsplits, int vps, int cu, int64_t kt) {
+  const int32_t spg = splits_per_run(R, nsplits, vps, cu);
+  const int64_t wgs = R * ((nsplits + spg - 1) / spg);
+  return (wgs + cu - 1) / cu * spg * vps * kt;
+}
+
+// Row-block height of a projection launch: 256 tokens, or 128 when 256-token
+// blocks give fewer workgroups than `cu` compute units and the 128-token
+// plan's K stages per compute unit, at 15/32 of the cost of a 256-token stage
+// (half the MFMA work and a deeper load pipeline), come out fewer.  K stages
+// per tile are ceil(H / 64) rounded up to the buffer count: 2 for 256-token
+// blocks, slots128 for 128-token blocks.  (Measured on MI355X: at H = 1024,
+// V = 32000, N = 512, one 256-token tile per workgroup, 250 workgroups,
+// takes 0.0386 ms against 0.042 ms for two 128-token tiles; at H = 4096,
+// V = 128256, 128-token blocks win for N <= 256, e.g. 0.184 against
+// 0.225 ms at N = 64.)  A row's arithmetic is the same in either (row blocking
+// never changes bits), so the choice may follow N, H and the device.
+int32_t row_block_rows(int64_t N, int64_t H, int64_t splits, int vps, int cu, int slots128) {
+  const int64_t r256 = (N + 255) / 256;
+  if (cu <= 0 || r256 * splits >= cu) return 256;
+  const int64_t k = (H + 63) / 64;
+  const int64_t kt256 = (k + 1) / 2 * 2;
+  const int64_t kt128 = (k + slots128 - 1) / slots128 * slots128;
+  const int64_t c256 = plan_stages(r256, (int)splits, vps, cu, kt256);
+  const int64_t c128 = plan_stages((N + 127) / 128, (int)splits, vps, cu, kt128);
+  return c128 * 15 < c256 * 32 ? 128 : 256;
 }
 
 int device_cus(int dev) { return g_cu_count[dev].load(std::memory_order_acquire); }
@@ -359,7 +381,7 @@ bilogp_status validate(const Call& c, int parts, bilogp::ProjParams* out) {
   // compute units the launch is scheduled for: the caller's count, else the
   // device's (row blocking and split runs never change a bit)
   const int cu = c.cu_count > 0 ? c.cu_count : device_cus(dev);
-  p.rows = row_block_rows(c.N, ranged ? c.split_end - c.split_begin : S, cu);
+  p.rows = row_block_rows(c.N, c.H, ranged ? c.split_end - c.split_begin : S, vps, cu, 3);
   p.hidden = c.hidden;
   // absolute-column addressing: shift the slice's base back by col0 columns
   // (unsigned arithmetic; the kernel adds them again before any access)
@@ -453,14 +475,15 @@ bilogp_status run(const Call& c, int parts, void* stream) {
 
 extern "C" {
 
-int bilogp_launch_plan(int64_t N, int64_t V, int mode, int cu_count, int* rows_per_block,
-                       int* splits_per_workgroup, int64_t* workgroups) {
-  if (N < 1 || N > kMaxN || V <= 0 || V > kMaxV || cu_count < 1 || cu_count > kMaxCuCount)
+int bilogp_launch_plan(int64_t N, int64_t H, int64_t V, int mode, int cu_count,
+                       int* rows_per_block, int* splits_per_workgroup, int64_t* workgroups) {
+  if (N < 1 || N > kMaxN || H < 1 || H > kMaxH || V <= 0 || V > kMaxV || cu_count < 1 ||
+      cu_count > kMaxCuCount)
     return -1;
   const int S = bilogp_num_vocab_splits_mode(N, V, mode, cu_count);
   const int vps = bilogp_vtiles_per_split_mode(N, V, mode, cu_count);
   if (S == 0 || vps == 0) return -1;
-  const int32_t rows = row_block_rows(N, S, cu_count);
+  const int32_t rows = row_block_rows(N, H, S, vps, cu_count, 3);
   const int64_t R = (N + rows - 1) / rows;
   const int32_t spg = splits_per_run(R, S, vps, cu_count);
   if (rows_per_block) *rows_per_block = rows;
@@ -816,7 +839,7 @@ bilogp_status bilogp_backward(const void* hidden, const void* weight, const int6
       p.T = (int32_t)((V + bilogp::kVtileCols - 1) / bilogp::kVtileCols);
       p.vps = bilogp_vtiles_per_split(V);
       p.S = bilogp_num_vocab_splits(V);
-      p.rows = row_block_rows(N, p.S, device_cus(dev));
+      p.rows = row_block_rows(N, H, p.S, p.vps, device_cus(dev), 2);
       p.R = (int32_t)((N + p.rows - 1) / p.rows);
       p.split0 = 0;
       p.split1 = p.S;

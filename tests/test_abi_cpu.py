@@ -36,13 +36,13 @@ def test_library_exports_every_declared_symbol():
 
 def test_constants_and_version():
     # ABI 2 added bilogp_bit_contract_version and the scheduling compute-unit
-    # count of the invariant mode.  Bit contract 2: tiles of 256 columns, at
+    # count of the invariant mode; ABI 3 added H to bilogp_launch_plan.  Bit contract 2: tiles of 256 columns, at
     # most 256 splits, the merge tree over consecutive per-lane split blocks
     # (contract 1 had at most 64 splits and lane-strided pre-sums).  Bit
     # contract 3: K in 32-wide steps of the 16 x 16 x 32 bf16 MFMA, per-token
     # sums over (lane group, register) of that tile layout.  Bit contract 4:
     # the deterministic GEMM and the backward's products on that MFMA too.
-    assert ila.bilogp_abi_version() == 2
+    assert ila.bilogp_abi_version() == 3
     assert ila.bilogp_bit_contract_version() == 4
     assert ila.bilogp_vtile_cols() == 256
     assert ila.bilogp_max_splits() == 256
@@ -552,7 +552,7 @@ def test_launch_plan_follows_the_compute_units_only_in_scheduling():
     V = 151936                                   # 594 tiles, 198 splits of 3
     cus = (1, 8, 32, 80, 128, 256, 304, 1024, 4096, 65536)
     for n in (1, 7, 300, 4096):
-        plans = {cu: ila.bilogp_launch_plan(n, V, inv, cu) for cu in cus}
+        plans = {cu: ila.bilogp_launch_plan(n, 4096, V, inv, cu) for cu in cus}
         for cu, (rows, spg, wgs) in plans.items():
             assert rows in (128, 256) and spg >= 1
             assert wgs == -(-n // rows) * -(-198 // spg)
@@ -560,12 +560,13 @@ def test_launch_plan_follows_the_compute_units_only_in_scheduling():
         assert plans[1][0] == 256 and plans[65536][0] == 128
         assert len(set(plans.values())) >= 2
     # at the headline V (2 tiles per split) the splits per workgroup follow the count too
-    hp = {cu: ila.bilogp_launch_plan(4096, 128256, inv, cu) for cu in (1, 100, 256, 1000)}
+    hp = {cu: ila.bilogp_launch_plan(4096, 4096, 128256, inv, cu) for cu in (1, 100, 256, 1000)}
     assert len({spg for _, spg, _ in hp.values()}) >= 2, hp
-    assert ila.bilogp_launch_plan(4096, 128256, inv, 256) == (256, 2, 16 * 126)
-    assert ila.bilogp_launch_plan(0, 1000, inv, 256) is None
-    assert ila.bilogp_launch_plan(8, 0, inv, 256) is None
-    assert ila.bilogp_launch_plan(8, 1000, inv, 0) is None
-    assert ila.bilogp_launch_plan(8, 1000, 7, 256) is None
+    assert ila.bilogp_launch_plan(4096, 4096, 128256, inv, 256) == (256, 2, 16 * 126)
+    assert ila.bilogp_launch_plan(0, 64, 1000, inv, 256) is None
+    assert ila.bilogp_launch_plan(8, 64, 0, inv, 256) is None
+    assert ila.bilogp_launch_plan(8, 0, 1000, inv, 256) is None
+    assert ila.bilogp_launch_plan(8, 64, 1000, inv, 0) is None
+    assert ila.bilogp_launch_plan(8, 64, 1000, 7, 256) is None
     # the throughput mode's split count follows the same count
-    assert ila.bilogp_launch_plan(8, 128256, tp, 256) is not None
+    assert ila.bilogp_launch_plan(8, 4096, 128256, tp, 256) is not None

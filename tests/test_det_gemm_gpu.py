@@ -163,8 +163,8 @@ def test_det_linear_autograd():
 
 def test_tile_sizes_give_the_same_bits():
     """A full batch with 256 x 256 tiles for every compute unit and row chunks
-    small enough for 128 x 128 tiles: the same rows, bit for bit (forward and
-    dA; every output is one MFMA chain whatever the tile)."""
+    small enough for 128 x 128 tiles: the same rows, bit for bit (forward, dA
+    and dB; every output is one MFMA chain whatever the tile)."""
     M, N, K = 4096, 4096, 256
     a, b = bf16((M, K), 17), bf16((N, K), 18)
     dc, b2 = bf16((M, 256), 19), bf16((256, 4096), 20)
@@ -174,6 +174,12 @@ def test_tile_sizes_give_the_same_bits():
     parts_c = [ila.det_gemm(a[i:i + 300], b, out_dtype=torch.float32) for i in range(0, M, 300)]
     parts_da = [ila.det_gemm_da(dc[i:i + 300], b2, out_dtype=torch.float32)
                 for i in range(0, M, 300)]
+    # dB (both operands read transposed): its rows n from column slices of dC
+    a3, dc3 = bf16((256, 4096), 21), bf16((256, 4096), 22)
+    full_db = ila.det_gemm_db(a3, dc3, out_dtype=torch.float32)   # 16 x 16 tiles of 256
+    parts_db = [ila.det_gemm_db(a3, dc3[:, i:i + 296].contiguous(), out_dtype=torch.float32)
+                for i in range(0, 4096, 296)]
     torch.cuda.synchronize()
     assert torch.equal(torch.cat(parts_c), full_c)
     assert torch.equal(torch.cat(parts_da), full_da)
+    assert torch.equal(torch.cat(parts_db), full_db)

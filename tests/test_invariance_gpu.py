@@ -176,7 +176,7 @@ def test_compute_unit_count_never_changes_bits(n):
     ref_lp, ref_ls = run_ex(h, w, t, b)
     plans = set()
     for cu in CU_COUNTS:
-        plans.add(ila.bilogp_launch_plan(n, V, ila.BILOGP_SPLITS_INVARIANT, cu))
+        plans.add(ila.bilogp_launch_plan(n, h.shape[1], V, ila.BILOGP_SPLITS_INVARIANT, cu))
         say(f"sweep n={n} cu_count={cu}")
         lp = torch.empty(n, device=DEV)
         ls = torch.empty(n, device=DEV)
