@@ -587,14 +587,17 @@ __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
             (void*)(p.dzt + (int64_t)vbase * p.ldz), (short)0, vrows * (int)p.ldz * 2,
             kRsrcWord3);
         uint32_t vo[kTj];
-        bool live[kTj];
         int trel[kTj];
         float lse_r[kTj], coef[kTj], gtg[kTj];
 #pragma unroll
         for (int tj = 0; tj < kTj; ++tj) {
           const int jr = wt * kWaveTok + tj * 16 + lr;
-          live[tj] = jr < rows_here;
-          vo[tj] = ((uint32_t)(wv * 128 + 4 * lg) * (uint32_t)p.ldz + (uint32_t)(m0 + jr)) * 2u;
+          // a token past the batch stores past the resource's end, where the
+          // range check drops it: no branch around the stores (kOutOfRange +
+          // 127 rows of at most 2^22 bytes stays below 2^32)
+          vo[tj] = jr < rows_here
+                       ? ((uint32_t)(wv * 128 + 4 * lg) * (uint32_t)p.ldz + (uint32_t)(m0 + jr)) * 2u
+                       : kOutOfRange;
           // opaque per tile: the store addresses are formed here, not hoisted
           // out of the stage loop into registers that would then spill
           asm volatile("" : "+v"(vo[tj]));
@@ -614,9 +617,8 @@ __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
             for (int tj = 0; tj < kTj; ++tj) {
               float dz = exp2_hw((acc[vi][tj][e] - lse_r[tj]) * kLog2e) * coef[tj];
               if (trel[tj] == k) dz += gtg[tj];
-              if (live[tj])
-                __builtin_amdgcn_raw_buffer_store_b16(bf16_rne(dz), rs_dz,
-                                                      vo[tj] + (uint32_t)k * ld2, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b16(bf16_rne(dz), rs_dz,
+                                                    vo[tj] + (uint32_t)k * ld2, 0, 0);
             }
           }
           __builtin_amdgcn_sched_barrier(0);
