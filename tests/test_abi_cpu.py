@@ -570,3 +570,21 @@ def test_launch_plan_follows_the_compute_units_only_in_scheduling():
     assert ila.bilogp_launch_plan(8, 64, 1000, 7, 256) is None
     # the throughput mode's split count follows the same count
     assert ila.bilogp_launch_plan(8, 4096, 128256, tp, 256) is not None
+
+
+def test_row_block_height_follows_the_stage_count():
+    """128-token blocks only where 256-token blocks leave compute units idle
+    AND the 128-token plan has fewer (weighted) K stages per unit: the plans
+    that measured fastest on MI355X at these shapes."""
+    inv = B.BILOGP_SPLITS_INVARIANT
+    plan = lambda n, h, v: ila.bilogp_launch_plan(n, h, v, inv, 256)
+    # medium configuration: one 256-token tile per workgroup beats two padded
+    # 128-token tiles (0.0337 against 0.0396 ms)
+    assert plan(512, 1024, 32000) == (256, 1, 250)
+    assert plan(256, 256, 151936)[0] == 256
+    # long contractions at small N: the 3-buffer 128-token pipeline wins
+    assert plan(64, 4096, 128256) == (128, 1, 251)
+    assert plan(256, 4096, 128256) == (128, 2, 252)
+    # 256-token blocks that fill the device are always kept
+    assert plan(4096, 4096, 128256) == (256, 2, 2016)
+    assert plan(1024, 1024, 32000) == (256, 2, 252)
