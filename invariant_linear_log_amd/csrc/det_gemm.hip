@@ -105,11 +105,12 @@ __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 // Chunk swizzle of a transposed slice row (see the LDS layouts above).
 __device__ __forceinline__ int htr(int row) { return 2 * ((row & 3) | (((row >> 3) & 1) << 2)); }
 
-// fp32 -> bf16, round to nearest even (NaN stays a quiet NaN).
+// fp32 -> bf16 bits, round to nearest even: gfx950's conversion instruction
+// (v_cvt_pk_bf16_f32).  fp32 denormals are kept (the kernels run with fp32
+// denormal mode on), so every finite value and infinity rounds exactly as
+// the IEEE definition; a NaN stays a NaN.
 __device__ __forceinline__ uint32_t bf16_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // A buffer resource over [base, base + bytes), built from values forced into

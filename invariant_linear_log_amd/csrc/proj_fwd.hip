@@ -126,11 +126,12 @@ __device__ __forceinline__ void merge_state(float m_lo, float s_lo, float m_hi, 
 template <int I>
 using Slot = std::integral_constant<int, I>;
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+// fp32 -> bf16 bits, round to nearest even: gfx950's conversion instruction
+// (v_cvt_pk_bf16_f32).  fp32 denormals are kept (the kernels run with fp32
+// denormal mode on), so every finite value and infinity rounds exactly as
+// the IEEE definition; a NaN stays a NaN.
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // The kernel body.  kTj token blocks of 16 per wave: 4 (256-token row
