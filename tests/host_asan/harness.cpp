@@ -248,8 +248,22 @@ static void proj_footprint(const ProjParams& p, bool grad) {
   }
 }
 
+// What the projection launches of one call looked like: row-block height and
+// splits per workgroup of the first launch, workgroups summed over row chunks.
+struct LaunchSeen {
+  int rows = 0, spg = 0, launches = 0;
+  int64_t workgroups = 0;
+} g_seen;
+
 hipError_t launch_proj_lse(const ProjParams& p, hipStream_t) {
   proj_footprint(p, false);
+  if (g_seen.launches++ == 0) {
+    g_seen.rows = p.rows;
+    g_seen.spg = p.spg;
+  } else if (g_seen.rows != p.rows || g_seen.spg != p.spg) {
+    g_seen.rows = -1;     // row chunks of one call must share the plan
+  }
+  g_seen.workgroups += (int64_t)p.R * p.S_grid;
   return hipSuccess;
 }
 
@@ -384,9 +398,23 @@ void forward_case(int64_t N, int64_t H, int64_t V, int bias_dtype, int mode, int
   g_bufs.ws = ws.span();
   g_bufs.n_total = N;
   const void* bias = bias_dtype == BILOGP_BIAS_NONE ? nullptr : b.p;
+  bilogp::g_seen = bilogp::LaunchSeen{};
   expect(bilogp_forward_mode(h.p, w.p, (const int64_t*)t.p, bias, bias_dtype, (float*)lp.p, (float*)ls.p, N, H,
                              V, mode, cu, ws.p, need, nullptr),
          BILOGP_OK, tag + " forward_mode");
+  if (N > 0 && cu > 0) {
+    // bilogp_launch_plan describes exactly what bilogp_forward_mode launched
+    int rows = 0, spg = 0;
+    int64_t wgs = 0;
+    if (bilogp_launch_plan(N, H, V, mode, cu, &rows, &spg, &wgs) != 0)
+      fail_now(tag + ": launch plan refused valid arguments");
+    const bilogp::LaunchSeen& seen = bilogp::g_seen;
+    if (rows != seen.rows || spg != seen.spg || wgs != seen.workgroups)
+      fail_now(tag + ": launch plan (" + std::to_string(rows) + ", " + std::to_string(spg) +
+                ", " + std::to_string(wgs) + ") differs from the launch (" +
+                std::to_string(seen.rows) + ", " + std::to_string(seen.spg) + ", " +
+                std::to_string(seen.workgroups) + ")");
+  }
   if (mode == BILOGP_SPLITS_INVARIANT) {
     expect(bilogp_forward_ex(h.p, w.p, (const int64_t*)t.p, bias, bias_dtype, (float*)lp.p, (float*)ls.p, N, H, V,
                              ws.p, need, nullptr),

@@ -2,8 +2,9 @@
 shifted weight / bias base of a vocabulary-range launch, row chunking) built
 with g++ under AddressSanitizer and UndefinedBehaviorSanitizer against a fake
 HIP runtime whose stand-in kernels touch exactly the bytes the real kernels
-would (tests/host_asan/).  CPU only.  Two planted mistakes in a copy of the
-host source must make the harness fail, so it is known to catch them."""
+would (tests/host_asan/).  CPU only.  Planted mistakes in a copy of the
+host source must make the harness fail, so it is known to catch them; so must
+a launch plan that disagrees with the launch."""
 
 import os
 import shutil
@@ -25,14 +26,28 @@ def _gxx():
     return gxx
 
 
+def _sanitizers_available(tmp_path):
+    """Whether g++ can build and run a trivial program with the sanitizers
+    (a missing runtime skips the tests; a broken harness must fail them)."""
+    src = tmp_path / "probe.cpp"
+    src.write_text("int main() { return 0; }\n")
+    exe = tmp_path / "probe"
+    r = subprocess.run([_gxx(), *FLAGS, str(src), "-o", str(exe)], capture_output=True, text=True)
+    if r.returncode != 0:
+        return False, r.stderr[-300:]
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    return r.returncode == 0, r.stderr[-300:]
+
+
 def _build(tmp_path, host_src, name):
+    ok, why = _sanitizers_available(tmp_path)
+    if not ok:
+        pytest.skip("g++ sanitizer runtime not available: " + why)
     exe = tmp_path / name
     cmd = [_gxx(), *FLAGS, "-I", FAKE, "-I", os.path.join(ROOT, "include"), "-I",
            os.path.join(ROOT, "invariant_linear_log_amd", "csrc"), str(host_src), HARNESS,
            "-o", str(exe)]
     r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0 and "asan" in r.stderr.lower():
-        pytest.skip("AddressSanitizer runtime not available: " + r.stderr[-300:])
     assert r.returncode == 0, r.stderr[-3000:]
     return exe
 
@@ -56,6 +71,10 @@ MUTATIONS = {
     # row chunks whose partials start one row late
     "chunk_partials_one_row_late": ("q.part = p.part + r0 * p.S;",
                                     "q.part = p.part + (r0 + 1) * p.S;"),
+    # a launch plan that counts the 128-token stages with two buffers instead of
+    # the three the forward launches with
+    "launch_plan_wrong_buffer_count": ("  const int32_t rows = row_block_rows(N, H, S, vps, cu_count, 3);",
+                                       "  const int32_t rows = row_block_rows(N, H, S, vps, cu_count, 2);"),
 }
 
 
