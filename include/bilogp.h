@@ -131,8 +131,10 @@ int bilogp_vtiles_per_split(int64_t V);
 int bilogp_num_vocab_splits(int64_t V);
 
 /* Bytes of device workspace bilogp_forward_ex needs for N rows and vocabulary
- * size V: the [N, S] partial (max, sum-exp) pairs and the [N] target logits,
- * each 256-byte aligned.  0 for N == 0; (size_t)-1 for invalid N or V. */
+ * size V: the [N, S] partial (max, sum-exp) pairs, the [N] target logits and
+ * an fp32 copy of the bias padded to whole 256-column tiles (reserved whether
+ * or not a call passes a bias), each 256-byte aligned.  0 for N == 0;
+ * (size_t)-1 for invalid N or V. */
 size_t bilogp_workspace_bytes(int64_t N, int64_t V);
 
 /* Split policies (RL-Kernel PR #337, description, "Why this happens" and its

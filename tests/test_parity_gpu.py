@@ -77,6 +77,58 @@ def test_large_dims_full(N, H, V, bias, seed):
     assert_parity(logp, lse, ref_lp, ref_ls, what=f"large N={N} H={H} V={V}")
 
 
+def test_weight_past_4gib():
+    """A weight of more than 2^32 bytes: V = 2^28 + 100 rows of the narrowest
+    allowed width H = 8, so the last 100 rows lie past every 32-bit byte offset
+    from the weight's base; 256 splits of 4097 tiles (the last of 3842), one
+    real K stage per tile.  Three rows (one ragged row block), targets in the
+    first tile, the ragged last tile and past the 2^32-byte mark, against the
+    fp64 oracle."""
+    N, H, V = 3, 8, (1 << 28) + 100
+    assert ila.bilogp_num_vocab_splits(V) == 256 and ila.bilogp_vtiles_per_split(V) == 4097
+    g = torch.Generator(device=DEV).manual_seed(2028)
+    w = (torch.randn(V, H, generator=g, device=DEV) * (1.0 / math.sqrt(H))).to(torch.bfloat16)
+    h = torch.randn(N, H, generator=g, device=DEV).to(torch.bfloat16)
+    t = torch.tensor([0, V - 1, V - 60], dtype=torch.int64, device=DEV)
+    say(f"weight past 4 GiB N={N} H={H} V={V} ({V * H * 2} bytes)")
+    logp, lse = run_ex(h, w, t)
+    torch.cuda.synchronize()
+    ref_lp, ref_ls = oracle.linear_logp(h.cpu(), w.cpu(), t.cpu())
+    assert_parity(logp, lse, ref_lp, ref_ls, what=f"weight past 4 GiB V={V}")
+
+
+def test_largest_vocabulary_counts_every_column_once():
+    """V = 2^30, the largest vocabulary the library accepts (H = 8, a 16 GiB
+    zero weight).  Every logit is 0, so each split's partial is (max 0, sum =
+    its column count): 4194304 = 2^22 for every one of the 256 splits, an
+    integer the fp32 sum holds exactly, so a column skipped or counted twice
+    anywhere shows in the partials bit for bit.  lse = ln 2^30 within 4 fp32
+    ulps, the same on every row."""
+    N, H, V = 3, 8, 1 << 30
+    S = ila.bilogp_num_vocab_splits(V)
+    assert S == 256 and ila.bilogp_vtiles_per_split(V) == 16384
+    g = torch.Generator().manual_seed(30)
+    h = torch.randn(N, H, generator=g).to(torch.bfloat16).to(DEV)
+    w = torch.zeros(V, H, dtype=torch.bfloat16, device=DEV)
+    t = torch.tensor([0, V // 2 + 7, V - 1], dtype=torch.int64, device=DEV)
+    logp = torch.empty(N, dtype=torch.float32, device=DEV)
+    lse = torch.empty(N, dtype=torch.float32, device=DEV)
+    ws = ila.workspace_for(N, V, DEV)
+    say(f"W=0 V=2^30 H={H} N={N}")
+    ila.bilogp_forward_ex(h, w, t, None, logp, lse, ws)
+    torch.cuda.synchronize()
+    del w
+    part = ws[:8 * N * S].view(torch.float32).view(N, S, 2).cpu()
+    assert torch.equal(part[..., 0], torch.zeros(N, S)), "a split's max is not 0"
+    assert torch.equal(part[..., 1], torch.full((N, S), float(1 << 22))), \
+        "a split's sum is not its column count"
+    lnv = math.log(V)
+    tol = 4 * float(np.spacing(np.float32(lnv)))
+    assert float((lse.double() - lnv).abs().max()) <= tol
+    assert torch.equal(lse, lse[:1].expand(N)), "lse bits differ across rows"
+    assert torch.equal(logp, -lse), "logp != -lse with all logits zero"
+
+
 def test_headline_full():
     """All 4096 rows of the headline workload against the fp64 oracle (about
     5 s of host BLAS), in the launch configuration the benchmark times."""
