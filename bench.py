@@ -291,16 +291,19 @@ def invariance_cost(h, t, w, b, steps=10, warmup=3, repeats=3):
     return res
 
 
-def det_gemm_leg(steps=10, warmup=3):
+def det_gemm_leg(steps=10, warmup=3, reps=5):
     """The deterministic GEMM (forward, dA, dB, and forward + dA + dB) at M = N = K
     = 4096 and at the three shapes of the page's own table (M x K x N = 128 x 128
     x 128, 256 x 512 x 512, 512 x 1024 x 1024), with torch's bf16 matmul
-    (hipBLASLt, not deterministic by contract) beside them."""
+    (hipBLASLt, not deterministic by contract) beside them.  Per shape, the five
+    runs alternate in `reps` rounds of `steps` calls; ms = median over the rounds."""
     import torch
     import invariant_linear_log_amd as ila
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev).manual_seed(11)
-    out = {"peak_tflops": PEAK_BF16_TFLOPS}
+    out = {"peak_tflops": PEAK_BF16_TFLOPS,
+           "protocol": f"per shape, the runs alternate in {reps} rounds of {steps} calls after "
+                       f"{warmup} warmup calls each; ms = median over the rounds"}
     for (M, N, K) in ((4096, 4096, 4096), (128, 128, 128), (256, 512, 512), (512, 1024, 1024)):
         a = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
         b = torch.randn((N, K), generator=g, device=dev).to(torch.bfloat16)
@@ -315,20 +318,25 @@ def det_gemm_leg(steps=10, warmup=3):
         runs = {"fwd": lambda: ila.det_gemm(a, b), "da": lambda: ila.det_gemm_da(dc, b),
                 "db": lambda: ila.det_gemm_db(a, dc), "fwd_bwd": fwd_bwd,
                 "torch_matmul_fwd": lambda: torch.matmul(a, bt)}
-        rec = {}
-        for name, fn in runs.items():
+        for fn in runs.values():
             for _ in range(warmup):
                 fn()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(steps):
-                fn()
-            e1.record()
-            e1.synchronize()
-            ms = e0.elapsed_time(e1) / steps
+        times = {name: [] for name in runs}
+        for _ in range(reps):                    # the runs alternate, round by round
+            for name, fn in runs.items():
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(steps):
+                    fn()
+                e1.record()
+                e1.synchronize()
+                times[name].append(e0.elapsed_time(e1) / steps)
+        rec = {}
+        for name, v in times.items():
+            ms = statistics.median(v)
             f = 3 * flops if name == "fwd_bwd" else flops
-            rec[name] = {"ms": ms, "tflops": f / ms / 1e9}
+            rec[name] = {"ms": ms, "ms_min": min(v), "tflops": f / ms / 1e9}
         rec["fwd"]["frac"] = rec["fwd"]["tflops"] / PEAK_BF16_TFLOPS
         out[f"M{M}_N{N}_K{K}"] = rec
     return out
@@ -418,17 +426,20 @@ def shard_share_leg(h, t, w, b, ranks=8, steps=10, warmup=3):
                           "frac": fn_ / ns_ms / 1e9 / PEAK_BF16_TFLOPS}}
 
 
-def library_context_leg(h, t, w, b, steps=10, warmup=3):
+def library_context_leg(h, t, w, b, step, stream, reps=5, steps=10, warmup=3):
     """Context, not the product: the same contraction through torch's bf16 matmul
     (hipBLASLt; z = hidden . W^T materialised as bf16 [N, V], no softmax), and the
     unfused path a caller would otherwise run (that matmul, the bias added in
     float32, a float32 logsumexp over V and a gather of the target logit).  Neither is batch-
-    invariant by contract."""
+    invariant by contract.  The fused step and the library GEMM alternate on one
+    stream, `reps` rounds of `steps` calls each, so both see the same clock and
+    power state; medians and minima over the rounds."""
     import torch
     h2 = h.reshape(-1, h.shape[-1])
     t2 = t.reshape(-1)
     N, H = h2.shape
     V = w.shape[0]
+    flops = 2.0 * N * H * V
 
     def gemm():
         return torch.matmul(h2, w.t())
@@ -439,19 +450,38 @@ def library_context_leg(h, t, w, b, steps=10, warmup=3):
             z = z + b.float()
         lse = torch.logsumexp(z, dim=-1)
         return z.gather(1, t2[:, None])[:, 0] - lse, lse
-    rec = {}
-    for name, fn in (("hipblaslt_gemm", gemm), ("unfused_matmul_logsumexp", unfused)):
-        for _ in range(warmup):
-            fn()
+
+    def timed(fn, n):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
+        e0.record(stream)
+        for _ in range(n):
             fn()
-        e1.record()
+        e1.record(stream)
         e1.synchronize()
-        ms = e0.elapsed_time(e1) / steps
-        rec[name] = {"ms": ms, "tflops": 2.0 * N * H * V / ms / 1e9}
+        return e0.elapsed_time(e1) / n
+
+    alternating = {"fused_step": step, "hipblaslt_gemm": gemm}
+    times = {name: [] for name in alternating}
+    with torch.cuda.stream(stream):
+        for fn in alternating.values():
+            for _ in range(warmup):
+                fn()
+        for _ in range(reps):
+            for name, fn in alternating.items():
+                times[name].append(timed(fn, steps))
+        for _ in range(warmup):
+            unfused()
+        unfused_ms = timed(unfused, steps)
+    rec = {}
+    for name, v in times.items():
+        v = sorted(v)
+        rec[name] = {"ms": statistics.median(v), "ms_min": v[0],
+                     "tflops": flops / statistics.median(v) / 1e9}
+    rec["unfused_matmul_logsumexp"] = {"ms": unfused_ms, "tflops": flops / unfused_ms / 1e9}
+    rec["protocol"] = (f"fused_step and hipblaslt_gemm alternate on one stream, {reps} rounds "
+                       f"of {steps} calls each after {warmup} warmup calls; ms = median over "
+                       f"the rounds; the unfused path once, {steps} calls")
     torch.cuda.empty_cache()
     return rec
 
@@ -623,7 +653,7 @@ def main():
     if not args.no_det_gemm:
         out["det_gemm"] = det_gemm_leg()
     if not args.no_library_context:
-        out["library_context"] = library_context_leg(h, t, w, b)
+        out["library_context"] = library_context_leg(h, t, w, b, step, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows)
     print(json.dumps(out), flush=True)
