@@ -294,3 +294,39 @@ def test_headline_sampled_parity():
     ah = np.abs(h)
     _within(gw[torch.as_tensor(vrows, device=DEV)].cpu().numpy(), ref_w,
             Bc.T @ ah + N * U * (bigc.T @ ah), "grad_weight rows")
+
+
+def test_buffers_past_4gib():
+    """V = 2^19 + 40, N = 4096, H = 2048: dZ^T ([V, 4096] bf16) and grad_weight
+    ([V, 2048] fp32) are each just over 2^32 bytes, so the last 40 vocabulary
+    rows of both lie past every 32-bit byte offset.  Sampled rows of the
+    kernel's dZ^T, of grad_weight (among them rows past the 2^32-byte mark)
+    and of grad_hidden against the oracle within the derived bound."""
+    N, H, V = 4096, 2048, (1 << 19) + 40
+    assert V * N * 2 > 1 << 32 and V * H * 4 > 1 << 32
+    inp, up = _inputs(N, H, V, 12)
+    t = inp["target"]
+    t[0], t[1] = V - 1, V - 20                  # targets past the mark
+    say(f"backward buffers past 4 GiB N={N} H={H} V={V}")
+    with torch.no_grad():
+        _, lse = ila.forward(inp["hidden"], inp["weight"], t)
+    gh, gw, _, ws = _run(inp, up, lse, bias_grad=False)
+    vrows = np.array([0, 255, 256, V - 41, V - 40, V - 20, V - 1])
+    vsel = torch.as_tensor(vrows, device=DEV)
+    dzt = _dzt(ws, N, V)[vsel].cpu()
+    gw_s = gw[vsel].cpu().numpy()
+    rows = np.array([0, 1, 2047, N - 1])
+    gh_s = gh[torch.as_tensor(rows, device=DEV)].cpu().numpy()
+    torch.cuda.synchronize()
+    del ws, gw
+    h, w, b, tt, ls, gl, gs = _f64(inp, up, lse)
+    ah, aW = np.abs(h), np.abs(w)
+    dzc, Bc = _bounds(h, w, b, tt, ls, gl, gs, np.arange(N), vrows)
+    _within(oracle.to_f64(dzt).T, dzc, Bc, "dZ^T rows (workspace)")
+    ref_w, _ = oracle.grad_weight_rows(h, w, tt, b, ls, gl, gs, cols=vrows)
+    bigc = np.abs(dzc) + Bc
+    _within(gw_s, ref_w, Bc.T @ ah + N * U * (bigc.T @ ah), "grad_weight rows")
+    ref_h = oracle.grad_hidden_rows(h, w, tt, b, ls, gl, gs, rows=rows)
+    dz, B = _bounds(h, w, b, tt, ls, gl, gs, rows, np.arange(V))
+    big = np.abs(dz) + B
+    _within(gh_s, ref_h, B @ aW + V * U * (big @ aW), "grad_hidden rows")
