@@ -292,12 +292,19 @@ def _cpu_forward_args(N=4, H=16, V=40):
                 logp_out=torch.zeros(N), lse_out=torch.zeros(N))
 
 
-@pytest.mark.parametrize("fn", ["bilogp_forward", "bilogp_forward_ex", "bilogp_forward_mode"])
-@pytest.mark.parametrize("case,exc", [
+_RAW_CASES = [
     ("hidden_fp32", TypeError), ("target_int32", TypeError), ("bias_bf16_plain", TypeError),
     ("bias_fp64", TypeError), ("hidden_3d", ValueError), ("hidden_noncontig", ValueError),
     ("weight_cols", ValueError), ("target_short", ValueError), ("bias_short", ValueError),
-    ("logp_short", ValueError), ("lse_fp64", TypeError), ("cpu", ValueError)])
+    ("logp_short", ValueError), ("lse_fp64", TypeError), ("cpu", ValueError)]
+
+
+# a bf16 bias is an error only for bilogp_forward, whose bias is fp32 by signature;
+# the calls with an explicit bias dtype accept it
+@pytest.mark.parametrize("fn,case,exc", [
+    (fn, case, exc)
+    for fn in ("bilogp_forward", "bilogp_forward_ex", "bilogp_forward_mode")
+    for case, exc in _RAW_CASES if case != "bias_bf16_plain" or fn == "bilogp_forward"])
 def test_raw_wrappers_check_what_pointers_stand_for(fn, case, exc):
     """The C-ABI wrappers check dtypes, shapes and layout before the library
     sees bare pointers (a bf16 bias read as fp32, an int32 target or a short
@@ -308,8 +315,6 @@ def test_raw_wrappers_check_what_pointers_stand_for(fn, case, exc):
     elif case == "target_int32":
         a["target"] = a["target"].int()
     elif case == "bias_bf16_plain":
-        if fn != "bilogp_forward":
-            pytest.skip("bf16 bias is valid for the calls with an explicit bias dtype")
         a["bias"] = torch.zeros(40, dtype=torch.bfloat16)
     elif case == "bias_fp64":
         a["bias"] = torch.zeros(40, dtype=torch.float64)
