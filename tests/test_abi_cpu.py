@@ -7,6 +7,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 import torch
 
@@ -593,3 +594,51 @@ def test_row_block_height_follows_the_stage_count():
     # 256-token blocks that fill the device are always kept
     assert plan(4096, 4096, 128256) == (256, 2, 2016)
     assert plan(1024, 1024, 32000) == (256, 2, 252)
+
+
+def _plan_model(N, H, V, cu):
+    """The launch-plan rules as documented in bilogp_host.cpp and include/bilogp.h,
+    restated: V-only splits; runs of up to 4 tiles chosen by whole rounds of one
+    workgroup per compute unit (ties to the longer run); 128-token row blocks only
+    when 256-token blocks leave units idle and the 128-token plan's K stages per
+    unit, at 15/32 of a 256-token stage, come out fewer (stages per tile rounded up
+    to 2 buffers for 256-token blocks, 3 for 128-token blocks)."""
+    T = -(-V // 256)
+    vps = -(-T // 256)
+    S = -(-T // vps)
+
+    def spr(R):
+        cap = min(max(1, 4 // vps), S)
+        best, best_len = 1, None
+        for g in range(1, cap + 1):
+            length = -(-(R * -(-S // g)) // cu) * g
+            if best_len is None or length <= best_len:
+                best, best_len = g, length
+        return best
+
+    def stages(R, kt):
+        g = spr(R)
+        return -(-(R * -(-S // g)) // cu) * g * vps * kt
+
+    r256 = -(-N // 256)
+    rows = 256
+    if r256 * S < cu:
+        k = -(-H // 64)
+        c256 = stages(r256, -(-k // 2) * 2)
+        c128 = stages(-(-N // 128), -(-k // 3) * 3)
+        rows = 128 if c128 * 15 < c256 * 32 else 256
+    R = -(-N // rows)
+    g = spr(R)
+    return rows, g, R * -(-S // g)
+
+
+def test_launch_plan_matches_its_stated_rules():
+    """2000 seeded (N, H, V, compute units) against the rules restated above."""
+    rng = np.random.default_rng(2024)
+    inv = B.BILOGP_SPLITS_INVARIANT
+    for _ in range(2000):
+        N = int(rng.choice([rng.integers(1, 600), rng.integers(1, 20000), rng.integers(1, 1 << 22)]))
+        H = int(rng.integers(1, 8193)) * 8
+        V = int(rng.choice([rng.integers(1, 5000), rng.integers(1, 300000), rng.integers(1, 1 << 30)]))
+        cu = int(rng.choice([rng.integers(1, 64), 80, 256, 304, rng.integers(1, 4096)]))
+        assert ila.bilogp_launch_plan(N, H, V, inv, cu) == _plan_model(N, H, V, cu), (N, H, V, cu)
