@@ -421,29 +421,77 @@ __device__ __forceinline__ void det_gemm_body(const GemmParams& g) {
     // let them land before the workgroup's LDS is released
     if constexpr (kLoader) wait_vmcnt<0>();
 
-    // ---- store: four consecutive p per (vi, tj), one 16-byte (fp32) or
-    // 8-byte (bf16) store (P is a multiple of 8, so a block of four is
-    // either wholly inside or wholly past P).
+    // ---- store through LDS.  The stage buffers are free now: the tile is
+    // written into them in output order (row q; the 16-byte chunks of a row
+    // swizzled by the row), then read back so that consecutive lanes hold
+    // consecutive chunks of one row, and stored 16 bytes per lane: every
+    // store instruction writes whole tile rows, where writing the
+    // accumulators' own layout (16 rows, 32 or 64 bytes each) stalled the
+    // load path.  P is a multiple of 8, so a chunk (8 bf16 or 4 fp32) is
+    // wholly inside or wholly past P.  fp32 tiles of 256 x 256 go in two
+    // passes of 128 rows.
+    __syncthreads();        // every wave is done with the stage buffers
+    auto epilogue = [&](auto esz_c) {
+      constexpr int kEsz = decltype(esz_c)::value;          // bytes per output element
+      constexpr int kRowB = kTP * kEsz;                     // bytes per tile row
+      constexpr int kC = kRowB / 16;                        // 16-byte chunks per row
+      constexpr int kRs = kSlotBytes / kRowB;               // rows per buffer
+      constexpr int kPR = 2 * kRs < kTQ ? 2 * kRs : kTQ;    // rows per pass
+      constexpr int kPasses = kTQ / kPR;
+      constexpr int kWaveRows = 16 * kTj;                   // rows a wave holds
+      constexpr int kRpi = 64 / kC;                         // rows per read instruction
+      constexpr int kReads = kPR / 8 / kRpi;                // reads per wave and pass
+      constexpr int kSwz = kC < 32 ? kC - 1 : 31;
+      static_assert(kC <= 64 && 64 % kC == 0 && kPR % kWaveRows == 0 &&
+                    kPR % (8 * kRpi) == 0 && kTQ % kPR == 0, "epilogue geometry");
+      auto lds_at = [&](int row, int byte) -> uint8_t* {    // row within the pass
+        const int r = row % kRs;
+        uint8_t* base = row < kRs ? slot0 : slot1;
+        return base + r * kRowB + (((byte >> 4) ^ (r & kSwz)) << 4) + (byte & 15);
+      };
 #pragma unroll
-    for (int tj = 0; tj < kTj; ++tj) {
-      const int64_t q = q0 + wt * 16 * kTj + tj * 16 + lr;
-      if (q >= g.Q) continue;
+      for (int pass = 0; pass < kPasses; ++pass) {
+        const int row_lo = pass * kPR;
+        if (wt * kWaveRows >= row_lo && wt * kWaveRows < row_lo + kPR) {
 #pragma unroll
-      for (int vi = 0; vi < kVi; ++vi) {
-        const int64_t p = p0 + wv * 16 * kVi + vi * 16 + 4 * lg;
-        if (p >= g.P) continue;
-        const floatx4 v = acc[vi][tj];
-        if (g.out_kind == kGemmBf16) {
-          uint16_t* o = (uint16_t*)g.out + q * g.ldo + p;
-          const uint2 w2 = {bf16_bits(v[0]) | (bf16_bits(v[1]) << 16),
-                            bf16_bits(v[2]) | (bf16_bits(v[3]) << 16)};
-          *(uint2*)o = w2;
-        } else {
-          floatx4* o = (floatx4*)((float*)g.out + q * g.ldo + p);
-          *o = g.out_kind == kGemmF32Accum ? *o + v : v;
+          for (int tj = 0; tj < kTj; ++tj)
+#pragma unroll
+            for (int vi = 0; vi < kVi; ++vi) {
+              const int row = wt * kWaveRows + tj * 16 + lr - row_lo;
+              const int pb = (wv * 16 * kVi + vi * 16 + 4 * lg) * kEsz;
+              const floatx4 v = acc[vi][tj];
+              if constexpr (kEsz == 2) {
+                const uint2 w2 = {bf16_bits(v[0]) | (bf16_bits(v[1]) << 16),
+                                  bf16_bits(v[2]) | (bf16_bits(v[3]) << 16)};
+                *(uint2*)lds_at(row, pb) = w2;
+              } else {
+                *(floatx4*)lds_at(row, pb) = v;
+              }
+            }
         }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kReads; ++k) {
+          const int row = wave * (kPR / 8) + k * kRpi + lane / kC;
+          const int c = lane % kC;
+          const uint4 d = *(const uint4*)lds_at(row, c * 16);
+          const int64_t q = q0 + row_lo + row;
+          const int64_t p = p0 + c * (16 / kEsz);
+          if (q < g.Q && p < g.P) {
+            uint8_t* o = (uint8_t*)g.out + (q * g.ldo + p) * kEsz;
+            if (kEsz == 4 && g.out_kind == kGemmF32Accum)
+              *(floatx4*)o = *(const floatx4*)o + __builtin_bit_cast(floatx4, d);
+            else
+              *(uint4*)o = d;
+          }
+        }
+        if (pass + 1 < kPasses) __syncthreads();
       }
-    }
+    };
+    if (g.out_kind == kGemmBf16)
+      epilogue(std::integral_constant<int, 2>{});
+    else
+      epilogue(std::integral_constant<int, 4>{});
   };
   if (loader)
     run(std::true_type{});

@@ -62,3 +62,72 @@ def test_transposed_slice_layout(kT):
                         r, c, _ = addr[src]
                         assert c + i % 4 == 16 * m + i            # the lane's own column
                         assert r == 32 * u + 8 * g + 4 * t + jj   # its contraction values
+
+
+@pytest.mark.parametrize("kVi,kTj,esz", [(8, 4, 2), (8, 4, 4), (4, 2, 2), (4, 2, 4)])
+def test_store_epilogue_layout(kVi, kTj, esz):
+    """The GEMM's store epilogue through LDS (det_gemm.hip): per pass, the waves
+    holding the pass's rows write each accumulator's four values to row q, byte
+    p * esz of the staging layout (16-byte chunk c of row r at position
+    c ^ (r & swz) inside buffer r // rows_per_buffer); every wave then reads 16
+    bytes per lane, lanes of one row taking its consecutive chunks.  Checked:
+    every staging byte of a pass is written exactly once and stays inside the
+    two stage buffers; the reads cover every (row, chunk) of the pass exactly
+    once and find there the values of output row q0 + row, columns
+    p0 + 16 c / esz .. + 16 / esz - 1; each read instruction covers whole rows."""
+    kTP, kTQ = 32 * kVi, 64 * kTj
+    slot_bytes = (kTP * 64 * 2) + (kTQ * 64 * 2)        # X slice + Y slice of a stage
+    row_b = kTP * esz
+    C = row_b // 16
+    Rs = slot_bytes // row_b
+    PR = min(2 * Rs, kTQ)
+    passes = kTQ // PR
+    wave_rows = 16 * kTj
+    rpi = 64 // C
+    reads = PR // 8 // rpi
+    swzm = C - 1 if C < 32 else 31
+    assert C <= 64 and 64 % C == 0 and PR % wave_rows == 0 and PR % (8 * rpi) == 0
+
+    def lds_at(row, byte):
+        r = row % Rs
+        base = 0 if row < Rs else slot_bytes
+        return base + r * row_b + (((byte >> 4) ^ (r & swzm)) << 4) + (byte & 15)
+
+    covered_q = set()
+    for ps in range(passes):
+        row_lo = ps * PR
+        owner = {}
+        for wave in range(8):
+            wv, wt = wave & 1, wave >> 1
+            if not (row_lo <= wt * wave_rows < row_lo + PR):
+                continue
+            for lane in range(64):
+                lr, lg = lane & 15, lane >> 4
+                for tj in range(kTj):
+                    for vi in range(kVi):
+                        row = wt * wave_rows + tj * 16 + lr - row_lo
+                        p = wv * 16 * kVi + vi * 16 + 4 * lg
+                        for i in range(4):
+                            for b in range(esz):
+                                a = lds_at(row, (p + i) * esz + b)
+                                assert 0 <= a < 2 * slot_bytes
+                                assert a not in owner
+                                owner[a] = (row_lo + row, p + i)      # (q, p) of the value
+        assert len(owner) == PR * row_b
+        seen = set()
+        for wave in range(8):
+            for k in range(reads):
+                rows_here = set()
+                for lane in range(64):
+                    row = wave * (PR // 8) + k * rpi + lane // C
+                    c = lane % C
+                    rows_here.add(row)
+                    assert (row, c) not in seen
+                    seen.add((row, c))
+                    for b in range(16):
+                        q, p = owner[lds_at(row, c * 16 + b)]
+                        assert q == row_lo + row and p == c * (16 // esz) + b // esz
+                    covered_q.add(row_lo + row)
+                assert len(rows_here) == rpi                 # whole rows per instruction
+        assert len(seen) == PR * C
+    assert covered_q == set(range(kTQ))
