@@ -92,6 +92,45 @@ def test_gradients_parity(M, N, K):
     check(db16, ref_db, s_db, M, torch.bfloat16, "dB bf16")
 
 
+def test_256_tiles_with_ragged_edges():
+    """Products large enough for 256 x 256 tiles on every compute unit (17 x 17
+    tiles) with the last tile row and column ragged, in all three layouts and
+    all output kinds: the store epilogue of the 256-tile kernels (whole rows
+    through LDS; fp32 in two passes) against the fp64 oracle."""
+    Mb, Nb, Kc = 4200, 4136, 520
+    # forward: C[4200, 4136] = A[4200, 520] . B[4136, 520]^T
+    a, b = bf16((Mb, Kc), 31), bf16((Nb, Kc), 32)
+    # dA[4200, 4136] = dC[4200, 520] . B2[520, 4136]
+    dc, b2 = bf16((Mb, Kc), 33), bf16((Kc, Nb), 34)
+    # dB[4200, 4136] = dC3[520, 4200]^T . A3[520, 4136]
+    a3, dc3 = bf16((Kc, Nb), 35), bf16((Kc, Mb), 36)
+    say("det_gemm 256-tile kernels, ragged edges")
+    c16 = ila.det_gemm(a, b)
+    c32 = ila.det_gemm(a, b, out_dtype=torch.float32)
+    init = torch.randn((Mb, Nb), generator=torch.Generator().manual_seed(37)).to(DEV)
+    acc = init.clone()
+    ila.det_gemm(a, b, out=acc, accumulate=True)
+    da16 = ila.det_gemm_da(dc, b2)
+    da32 = ila.det_gemm_da(dc, b2, out_dtype=torch.float32)
+    db16 = ila.det_gemm_db(a3, dc3)
+    db32 = ila.det_gemm_db(a3, dc3, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.det_gemm_fwd(a.cpu(), b.cpu())
+    s = oracle.abs_product("fwd", a.cpu(), b.cpu())
+    check(c16, ref, s, Kc, torch.bfloat16, "fwd bf16, 256 tiles")
+    check(c32, ref, s, Kc, torch.float32, "fwd fp32, 256 tiles")
+    check(acc, ref + init.double().cpu().numpy(), s, Kc + 1, torch.float32,
+          "fwd fp32 accumulate, 256 tiles", extra=U * np.abs(init.double().cpu().numpy()))
+    ref = oracle.det_gemm_da(dc.cpu(), b2.cpu())
+    s = oracle.abs_product("da", dc.cpu(), b2.cpu())
+    check(da16, ref, s, Kc, torch.bfloat16, "dA bf16, 256 tiles")
+    check(da32, ref, s, Kc, torch.float32, "dA fp32, 256 tiles")
+    ref = oracle.det_gemm_db(a3.cpu(), dc3.cpu())
+    s = oracle.abs_product("db", a3.cpu(), dc3.cpu())
+    check(db16, ref, s, Kc, torch.bfloat16, "dB bf16, 256 tiles")
+    check(db32, ref, s, Kc, torch.float32, "dB fp32, 256 tiles")
+
+
 @pytest.mark.parametrize("chunk", [1, 7, 256, 300])
 def test_rows_do_not_depend_on_the_batch(chunk):
     """Forward and dA rows: the full batch equals the concatenation of
