@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define BILOGP_ABI_VERSION 3
+#define BILOGP_ABI_VERSION 4
 
 /* Version of the bit contract: for given inputs of one row (its hidden row
  * and target, W, bias, H, V), which fp32 bits logp and lse take, and for the
@@ -177,12 +177,25 @@ size_t bilogp_workspace_bytes_mode(int64_t N, int64_t V, int mode, int cu_count)
  * scheduled for cu_count compute units (what bilogp_forward_mode does with
  * the same arguments): tokens per row block (256, or 128 when 256-token
  * blocks would leave units idle and the 128-token plan has the shorter
- * critical path), consecutive splits per workgroup, and the workgroup count.
+ * critical path), consecutive splits per workgroup (of the longest runs),
+ * and the workgroup count of all its launches (bilogp_launch_schedule).
  * Scheduling only - in the invariant mode no output bit depends on it.
  * Host-side, no device needed.  Returns 0, or -1 for N < 1, H, V or cu_count
  * out of range, or an unknown mode (outputs untouched).  (ABI 3 added H.) */
 int bilogp_launch_plan(int64_t N, int64_t H, int64_t V, int mode, int cu_count,
                        int* rows_per_block, int* splits_per_workgroup, int64_t* workgroups);
+
+/* Split schedule of the same plan, for S splits.  With 256-token row blocks,
+ * splits [0, split_a) go in runs of splits_per_workgroup, [split_a, split_t)
+ * one per workgroup, both in one launch, and [split_t, S) to a second launch
+ * of 128-token row blocks, one split per workgroup: the big launch ends after
+ * whole rounds of one workgroup per compute unit and the remainder fills one
+ * round of half-height pieces.  It is chosen where a cost model of K stages
+ * per compute unit has it ending first; otherwise split_a = split_t = S.
+ * Scheduling only, as above.  Returns 0 or -1 as bilogp_launch_plan.
+ * (ABI 4.) */
+int bilogp_launch_schedule(int64_t N, int64_t H, int64_t V, int mode, int cu_count,
+                           int* split_a, int* split_t);
 
 /* Fused forward with an optional fp32 bias and a library-managed workspace
  * (stream-ordered hipMallocAsync / hipFreeAsync on `stream`).

@@ -58,6 +58,7 @@ from ._binding import (  # noqa: F401
     bilogp_forward_noalloc,
     bilogp_last_error,
     bilogp_launch_plan,
+    bilogp_launch_schedule,
     bilogp_max_splits,
     bilogp_merge,
     bilogp_noalloc_max_workspace_bytes,

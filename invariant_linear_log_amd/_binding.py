@@ -55,6 +55,9 @@ SIGNATURES = {
     "bilogp_launch_plan": (ctypes.c_int, [_I64, _I64, _I64, ctypes.c_int, ctypes.c_int,
                                           ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
                                           ctypes.POINTER(ctypes.c_int64)]),
+    "bilogp_launch_schedule": (ctypes.c_int, [_I64, _I64, _I64, ctypes.c_int, ctypes.c_int,
+                                              ctypes.POINTER(ctypes.c_int),
+                                              ctypes.POINTER(ctypes.c_int)]),
     "bilogp_forward_mode": (ctypes.c_int, [_VP, _VP, _VP, _VP, ctypes.c_int, _VP, _VP, _I64, _I64,
                                            _I64, ctypes.c_int, ctypes.c_int, _VP,
                                            ctypes.c_size_t, _VP]),
@@ -239,6 +242,15 @@ def bilogp_launch_plan(N: int, H: int, V: int, mode: int, cu_count: int):
     st = load_library().bilogp_launch_plan(N, H, V, mode, cu_count, ctypes.byref(rows),
                                            ctypes.byref(spg), ctypes.byref(wgs))
     return None if st != 0 else (rows.value, spg.value, wgs.value)
+
+
+def bilogp_launch_schedule(N: int, H: int, V: int, mode: int, cu_count: int):
+    """(split_a, split_t) of the projection's split schedule, or None for
+    invalid arguments."""
+    a, t = ctypes.c_int(), ctypes.c_int()
+    st = load_library().bilogp_launch_schedule(N, H, V, mode, cu_count, ctypes.byref(a),
+                                               ctypes.byref(t))
+    return None if st != 0 else (a.value, t.value)
 
 
 def bilogp_status_string(status: int) -> str:

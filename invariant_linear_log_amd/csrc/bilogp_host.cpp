@@ -150,7 +150,113 @@ int32_t row_block_rows(int64_t N, int64_t H, int64_t splits, int vps, int cu, in
   return c128 * 15 < c256 * 32 ? 128 : 256;
 }
 
+// Schedule of a launch of 256-token row blocks over ns splits of vps tiles:
+// splits [0, sa) in runs of spg, [sa, sb) one per workgroup, and [sb, ns) in
+// a second launch of 128-token row blocks.  The last round of one workgroup
+// per compute unit is what it improves: with R * ns = q * cu + r splits,
+// q whole rounds plus r left over, the plain launch (sb = sa = ns) pays a
+// whole round for the r; here the big launch stops after whole rounds and
+// the r splits, cut in two halves of 128 tokens, fill one round of half
+// pieces.  A row's arithmetic is the same in either row-block height, so
+// the schedule never changes a bit.  Cost model, in 256-token K stages per
+// compute unit: kt256 per tile, 19/32 of one per 128-token stage (measured on
+// MI355X with every unit busy: 3.56 ms for 128-token blocks against 2.95 ms
+// for 256-token blocks at N = H = 4096, V = 128256, one tile per split), one
+// stage per workgroup start (measured: runs of 1 tile instead of 4 cost
+// 1.2% there) and three for the second launch.  Runs of single splits
+// between the long runs and the short pieces (at least three rounds of
+// them) level the end of the big launch.
+struct Schedule {
+  int32_t spg, sa, sb;
+};
+
+Schedule schedule_256(int64_t R, int ns, int vps, int cu, int64_t kt256, int64_t kt128) {
+  const int32_t spg = splits_per_run(R, ns, vps, cu);
+  Schedule best{spg, ns, ns};
+  if (cu <= 0 || R * ns <= cu) return best;
+  auto cdiv = [](int64_t a, int64_t b) { return (a + b - 1) / b; };
+  const int64_t wgs = R * cdiv(ns, spg);
+  int64_t best_cost = 32 * (cdiv(wgs, cu) * spg * vps * kt256 + cdiv(wgs, cu));
+  const int32_t cap = std::min(std::max(1, kTilesPerRun / std::max(vps, 1)), ns);
+  const int64_t b_min = cdiv(3 * (int64_t)cu, R);       // splits per row block in phase B
+  for (int64_t ts = 1; ts < ns && 2 * R * ts <= cu; ++ts) {
+    const int64_t sb = ns - ts;
+    const int64_t sa = std::max<int64_t>(0, sb - b_min) / cap * cap;
+    const int64_t starts = cdiv(R * (sa / cap), cu) + cdiv(R * (sb - sa), cu) + 1;
+    const int64_t cost = 32 * (cdiv(R * sb, cu) * vps * kt256 + starts + 3) + 19 * vps * kt128;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = Schedule{sa > 0 ? cap : 1, (int32_t)sa, (int32_t)sb};
+    }
+  }
+  return best;
+}
+
 int device_cus(int dev) { return g_cu_count[dev].load(std::memory_order_acquire); }
+
+// Workgroups a launch may have (the grid stays within 32-bit work-item
+// counts); a call with more row blocks x splits keeps the one-phase schedule
+// and is issued in row chunks.
+constexpr int64_t kMaxLaunchBlocks = (int64_t)(UINT32_MAX / 512u);
+
+// Row blocking and schedule of a projection over splits [p.split0, p.split1)
+// of p.vps tiles each (p.N and p.H set).
+void plan_projection(bilogp::ProjParams& p, int cu, int slots128) {
+  const int ns = p.split1 - p.split0;
+  p.rows = row_block_rows(p.N, p.H, ns, p.vps, cu, slots128);
+  p.R = (int32_t)((p.N + p.rows - 1) / p.rows);
+  Schedule sc{splits_per_run(p.R, ns, p.vps, cu), ns, ns};
+  if (p.rows == 256 && (int64_t)p.R * ns <= kMaxLaunchBlocks) {
+    const int64_t k = ((int64_t)p.H + 63) / 64;
+    sc = schedule_256(p.R, ns, p.vps, cu, (k + 1) / 2 * 2, (k + 2) / 3 * 3);
+  }
+  p.spg = sc.spg;
+  p.splitA = p.split0 + sc.sa;
+  p.splitT = p.split0 + sc.sb;
+  p.runsA = (sc.sa + sc.spg - 1) / sc.spg;
+}
+
+// The launches of a planned projection: the 256-token (or 128-token) launch
+// over [split0, splitT) and, if splitT < split1, the 128-token launch over
+// [splitT, split1), single splits.
+bilogp::ProjParams main_launch(const bilogp::ProjParams& p) {
+  bilogp::ProjParams q = p;
+  q.split1 = p.splitT;
+  return q;
+}
+bilogp::ProjParams tail_launch(const bilogp::ProjParams& p) {
+  bilogp::ProjParams q = p;
+  q.rows = 128;
+  q.R = (int32_t)((p.N + 127) / 128);
+  q.split0 = p.splitT;
+  q.splitA = p.split1;
+  q.splitT = p.split1;
+  q.spg = 1;
+  q.runsA = p.split1 - p.splitT;
+  return q;
+}
+
+// The plan bilogp_forward_mode makes for these arguments (no device needed);
+// false for arguments it would refuse.
+bool plan_for(int64_t N, int64_t H, int64_t V, int mode, int cu_count, bilogp::ProjParams* out) {
+  if (N < 1 || N > kMaxN || H < 1 || H > kMaxH || V <= 0 || V > kMaxV || cu_count < 1 ||
+      cu_count > kMaxCuCount)
+    return false;
+  const int S = bilogp_num_vocab_splits_mode(N, V, mode, cu_count);
+  const int vps = bilogp_vtiles_per_split_mode(N, V, mode, cu_count);
+  if (S == 0 || vps == 0) return false;
+  bilogp::ProjParams& p = *out;
+  p.N = N;
+  p.H = (int32_t)H;
+  p.V = (int32_t)V;
+  p.vps = vps;
+  p.S = S;
+  p.split0 = 0;
+  p.split1 = S;
+  plan_projection(p, cu_count, 3);
+  return true;
+}
+
 
 bilogp_status check_on_device(const void* ptr, int dev, const char* name) {
   hipPointerAttribute_t attr;
@@ -381,7 +487,6 @@ bilogp_status validate(const Call& c, int parts, bilogp::ProjParams* out) {
   // compute units the launch is scheduled for: the caller's count, else the
   // device's (row blocking and split runs never change a bit)
   const int cu = c.cu_count > 0 ? c.cu_count : device_cus(dev);
-  p.rows = row_block_rows(c.N, c.H, ranged ? c.split_end - c.split_begin : S, vps, cu, 3);
   p.hidden = c.hidden;
   // absolute-column addressing: shift the slice's base back by col0 columns
   // (unsigned arithmetic; the kernel adds them again before any access)
@@ -402,11 +507,9 @@ bilogp_status validate(const Call& c, int parts, bilogp::ProjParams* out) {
   p.T = (int32_t)((c.V + bilogp::kVtileCols - 1) / bilogp::kVtileCols);
   p.vps = vps;
   p.S = S;
-  p.R = (int32_t)((c.N + p.rows - 1) / p.rows);
   p.split0 = ranged ? c.split_begin : 0;
   p.split1 = ranged ? c.split_end : S;
-  p.spg = splits_per_run(p.R, p.split1 - p.split0, p.vps, cu);
-  p.S_grid = (p.split1 - p.split0 + p.spg - 1) / p.spg;
+  plan_projection(p, cu, 3);
   p.col0 = col0;
   return BILOGP_OK;
 }
@@ -414,11 +517,11 @@ bilogp_status validate(const Call& c, int parts, bilogp::ProjParams* out) {
 // Every grid stays within 32-bit work-item counts: the projection and the
 // merge are issued in row chunks.  Rows are independent and a row's
 // arithmetic does not depend on the rows around it, so chunking never changes
-// a bit.  Projection: 512 work-items per workgroup, S_grid workgroups per row
-// block.  Merge: 64 work-items per row.
+// a bit.  Projection: 512 work-items per workgroup, runsA + split1 - splitA
+// workgroups per row block.  Merge: 64 work-items per row.
 int64_t proj_chunk_rows(const bilogp::ProjParams& p) {
-  const int64_t max_blocks = (int64_t)(UINT32_MAX / 512u);
-  return std::max<int64_t>(1, max_blocks / std::max(p.S_grid, 1)) * p.rows;
+  const int64_t per_rb = p.runsA + p.split1 - p.splitA;
+  return std::max<int64_t>(1, kMaxLaunchBlocks / std::max<int64_t>(per_rb, 1)) * p.rows;
 }
 constexpr int64_t kMergeChunkRows = int64_t(1) << 25;
 
@@ -437,9 +540,10 @@ bilogp_status launch(const bilogp::ProjParams& p, const Call& c, int parts, void
       return fail(BILOGP_E_HIP, std::string("bias copy launch: ") + hipGetErrorString(e));
   }
   if (parts & kProj) {
-    const int64_t chunk = proj_chunk_rows(p);
-    for (int64_t r0 = 0; r0 < p.N; r0 += chunk) {
-      bilogp::ProjParams q = p;
+    const bilogp::ProjParams m = main_launch(p);
+    const int64_t chunk = proj_chunk_rows(m);
+    for (int64_t r0 = 0; r0 < p.N && m.split1 > m.split0; r0 += chunk) {
+      bilogp::ProjParams q = m;
       q.N = std::min(chunk, p.N - r0);
       q.R = (int32_t)((q.N + p.rows - 1) / p.rows);
       q.hidden = static_cast<const uint16_t*>(p.hidden) + r0 * p.H;
@@ -447,6 +551,12 @@ bilogp_status launch(const bilogp::ProjParams& p, const Call& c, int parts, void
       q.part = p.part + r0 * p.S;
       q.tlogit = p.tlogit + r0;
       hipError_t e = bilogp::launch_proj_lse(q, s);
+      if (e != hipSuccess)
+        return fail(BILOGP_E_HIP, std::string("projection launch: ") + hipGetErrorString(e));
+    }
+    if (p.splitT < p.split1) {
+      // the planner only makes a second launch when one launch holds the first
+      hipError_t e = bilogp::launch_proj_lse(tail_launch(p), s);
       if (e != hipSuccess)
         return fail(BILOGP_E_HIP, std::string("projection launch: ") + hipGetErrorString(e));
     }
@@ -477,18 +587,27 @@ extern "C" {
 
 int bilogp_launch_plan(int64_t N, int64_t H, int64_t V, int mode, int cu_count,
                        int* rows_per_block, int* splits_per_workgroup, int64_t* workgroups) {
-  if (N < 1 || N > kMaxN || H < 1 || H > kMaxH || V <= 0 || V > kMaxV || cu_count < 1 ||
-      cu_count > kMaxCuCount)
-    return -1;
-  const int S = bilogp_num_vocab_splits_mode(N, V, mode, cu_count);
-  const int vps = bilogp_vtiles_per_split_mode(N, V, mode, cu_count);
-  if (S == 0 || vps == 0) return -1;
-  const int32_t rows = row_block_rows(N, H, S, vps, cu_count, 3);
-  const int64_t R = (N + rows - 1) / rows;
-  const int32_t spg = splits_per_run(R, S, vps, cu_count);
-  if (rows_per_block) *rows_per_block = rows;
-  if (splits_per_workgroup) *splits_per_workgroup = spg;
-  if (workgroups) *workgroups = R * ((S + spg - 1) / spg);
+  bilogp::ProjParams p{};
+  if (!plan_for(N, H, V, mode, cu_count, &p)) return -1;
+  if (rows_per_block) *rows_per_block = p.rows;
+  if (splits_per_workgroup) *splits_per_workgroup = p.spg;
+  if (workgroups) {
+    const bilogp::ProjParams m = main_launch(p);
+    *workgroups = (int64_t)m.R * (m.runsA + m.split1 - m.splitA);
+    if (p.splitT < p.split1) {
+      const bilogp::ProjParams t = tail_launch(p);
+      *workgroups += (int64_t)t.R * (t.runsA + t.split1 - t.splitA);
+    }
+  }
+  return 0;
+}
+
+int bilogp_launch_schedule(int64_t N, int64_t H, int64_t V, int mode, int cu_count,
+                           int* split_a, int* split_t) {
+  bilogp::ProjParams p{};
+  if (!plan_for(N, H, V, mode, cu_count, &p)) return -1;
+  if (split_a) *split_a = p.splitA;
+  if (split_t) *split_t = p.splitT;
   return 0;
 }
 
@@ -839,19 +958,18 @@ bilogp_status bilogp_backward(const void* hidden, const void* weight, const int6
       p.T = (int32_t)((V + bilogp::kVtileCols - 1) / bilogp::kVtileCols);
       p.vps = bilogp_vtiles_per_split(V);
       p.S = bilogp_num_vocab_splits(V);
-      p.rows = row_block_rows(N, H, p.S, p.vps, device_cus(dev), 2);
-      p.R = (int32_t)((N + p.rows - 1) / p.rows);
       p.split0 = 0;
       p.split1 = p.S;
-      p.spg = splits_per_run(p.R, p.S, p.vps, device_cus(dev));
-      p.S_grid = (p.S + p.spg - 1) / p.spg;
+      plan_projection(p, device_cus(dev), 3);
       p.col0 = 0;
       p.lse = lse;
       p.g_logp = grad_logp;
       p.g_lse = grad_lse;
       p.dzt = dzt;
       p.ldz = ldz;
-      e = bilogp::launch_softmax_grad(p, s);
+      e = bilogp::launch_softmax_grad(main_launch(p), s);
+      if (e == hipSuccess && p.splitT < p.split1)
+        e = bilogp::launch_softmax_grad(tail_launch(p), s);
     }
     if (e == hipSuccess) {
       // grad_hidden[n][h] = sum over v ascending of dZ^T[v][n] W[v][h]

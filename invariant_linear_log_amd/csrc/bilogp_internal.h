@@ -36,17 +36,23 @@ struct ProjParams {
   int32_t S;               // splits
   int32_t rows;            // tokens per row block: 256, or 128 for small batches
   int32_t R;               // row blocks, ceil(N / rows)
-  // the launch covers splits [split0, split1) of the S, in runs of spg
-  // consecutive splits per workgroup (S_grid = ceil((split1 - split0) / spg)
-  // runs; the last may be shorter).  weight and
+  // the launch covers splits [split0, split1) of the S in two phases: per
+  // row block, runsA runs of spg consecutive splits over [split0, splitA)
+  // (runsA = ceil((splitA - split0) / spg); the last run may be shorter),
+  // then single splits over [splitA, split1); R * (runsA + split1 - splitA)
+  // workgroups.  A one-phase launch has splitA = split1.  weight and
   // bias are addressed by absolute vocabulary column: for a launch whose
   // weight holds columns from col0 on, the host passes the weight address
   // minus col0 rows (and the bias copy's address minus col0 entries); every
   // address the kernel forms stays inside the slice
   int32_t split0;
+  int32_t splitA;
   int32_t split1;
   int32_t spg;
-  int32_t S_grid;
+  int32_t runsA;
+  // host only: splits [splitT, split1) of the call go to a second launch of
+  // 128-token row blocks (splitT = split1: none)
+  int32_t splitT;
   int64_t col0;
   // backward only (softmax-gradient kernel): the forward's lse, the upstream
   // gradients of logp and lse, and dZ^T [V, ldz] (bf16) written per tile

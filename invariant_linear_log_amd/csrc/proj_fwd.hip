@@ -184,21 +184,31 @@ __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
   const int lg = lane >> 4;          // lane group: vocabulary rows 4 lg .. 4 lg + 3
 
   // Block id -> (split run, row block); a bijection that only orders the
-  // work.  Blocks go to the eight XCDs round-robin: first give each XCD a
-  // contiguous run of tile indices, then order tiles in groups of
+  // work.  A launch has up to two phases, longest work first: workgroups
+  // [0, R * runsA) take runs of spg consecutive splits of [split0, splitA),
+  // the rest single splits of [splitA, split1), so units that finish a long
+  // run early pick up short pieces and the last round ends nearly level.
+  // Within a phase, blocks go to the eight XCDs round-robin: first give each
+  // XCD a contiguous run of tile indices, then order tiles in groups of
   // kRowBlockGroup row blocks x all split runs (row blocks fastest), so the
   // ~32 tiles an XCD runs at once share a few W slices and a few hidden
   // blocks in its L2.
-  const int nblk = p.R * p.S_grid;
+  const int nA = p.R * p.runsA;
+  const bool ph_b = (int)blockIdx.x >= nA;
+  const int s_lo = ph_b ? p.splitA : p.split0;
+  const int s_hi = ph_b ? p.split1 : p.splitA;
+  const int spg = ph_b ? 1 : p.spg;
+  const int sg = ph_b ? p.split1 - p.splitA : p.runsA;      // runs per row block
+  const int nblk = p.R * sg;
   const int per_xcd = nblk >> 3;
-  int u = blockIdx.x;
+  int u = ph_b ? (int)blockIdx.x - nA : (int)blockIdx.x;
   if (u < (per_xcd << 3)) u = (u & 7) * per_xcd + (u >> 3);
-  const int in_group = kRowBlockGroup * p.S_grid;
+  const int in_group = kRowBlockGroup * sg;
   const int first_rb = (u / in_group) * kRowBlockGroup;
   const int group_rbs = min(p.R - first_rb, kRowBlockGroup);
   const int rb = first_rb + (u % in_group) % group_rbs;
-  const int split_first = p.split0 + (u % in_group) / group_rbs * p.spg;
-  const int split_last = min(split_first + p.spg, p.split1);     // exclusive
+  const int split_first = s_lo + (u % in_group) / group_rbs * spg;
+  const int split_last = min(split_first + spg, s_hi);          // exclusive
 
   const int64_t m0 = (int64_t)rb * kRows;
   const int rows_here = (int)min((int64_t)kRows, p.N - m0);
@@ -725,7 +735,7 @@ __global__ __launch_bounds__(kThreads, 1) void softmax_grad_bias_r128_kernel(con
 }  // namespace
 
 hipError_t launch_softmax_grad(const ProjParams& p, hipStream_t stream) {
-  const int64_t blocks = (int64_t)p.R * p.S_grid;
+  const int64_t blocks = (int64_t)p.R * (p.runsA + p.split1 - p.splitA);
   if (blocks <= 0) return hipSuccess;
   const bool bias = p.bias_kind != kBiasNone;
   auto k = p.rows == 128 ? (bias ? softmax_grad_bias_r128_kernel : softmax_grad_r128_kernel)
@@ -735,7 +745,7 @@ hipError_t launch_softmax_grad(const ProjParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_proj_lse(const ProjParams& p, hipStream_t stream) {
-  const int64_t blocks = (int64_t)p.R * p.S_grid;
+  const int64_t blocks = (int64_t)p.R * (p.runsA + p.split1 - p.splitA);
   if (blocks <= 0) return hipSuccess;
   const bool bias = p.bias_kind != kBiasNone;
   auto k = p.rows == 128 ? (bias ? proj_lse_bias_r128_kernel : proj_lse_r128_kernel)

@@ -146,25 +146,76 @@ Span ws_span_for(const void* p) {
 }
 
 // Workgroup -> (row block, split run): the projection kernel's block order
-// (blocks round-robin over eight XCDs, then groups of four row blocks x all
-// split runs), restated here to check it is a bijection for every launch.
-void check_block_order(int R, int S_grid) {
-  const int nblk = R * S_grid;
-  std::vector<uint8_t> seen((size_t)nblk, 0);
-  const int per_xcd = nblk >> 3;
-  for (int b = 0; b < nblk; ++b) {
-    int u = b;
+// (a phase of runs of spg splits over [split0, splitA), then one of single
+// splits over [splitA, split1); in each, blocks round-robin over eight XCDs,
+// then groups of four row blocks x all runs), restated here to check that
+// every launch visits each (row block, split) of its range exactly once.
+struct BlockWork {
+  int rb, split_first, split_last;
+};
+
+std::vector<BlockWork> block_order(const bilogp::ProjParams& p) {
+  if (p.split0 > p.splitA || p.splitA > p.split1) fail_now("phase bounds");
+  if (p.runsA != (p.splitA - p.split0 + p.spg - 1) / p.spg) fail_now("phase A run count");
+  const int nA = p.R * p.runsA;
+  const int nblk_all = nA + p.R * (p.split1 - p.splitA);
+  std::vector<BlockWork> out;
+  std::vector<uint8_t> seen((size_t)p.R * (p.split1 - p.split0), 0);
+  for (int b = 0; b < nblk_all; ++b) {
+    const bool ph_b = b >= nA;
+    const int s_lo = ph_b ? p.splitA : p.split0;
+    const int s_hi = ph_b ? p.split1 : p.splitA;
+    const int spg = ph_b ? 1 : p.spg;
+    const int sg = ph_b ? p.split1 - p.splitA : p.runsA;
+    const int nblk = p.R * sg;
+    const int per_xcd = nblk >> 3;
+    int u = ph_b ? b - nA : b;
     if (u < (per_xcd << 3)) u = (u & 7) * per_xcd + (u >> 3);
-    const int in_group = 4 * S_grid;
+    const int in_group = 4 * sg;
     const int first_rb = (u / in_group) * 4;
-    const int group_rbs = std::min(R - first_rb, 4);
+    const int group_rbs = std::min(p.R - first_rb, 4);
     const int rb = first_rb + (u % in_group) % group_rbs;
-    const int run = (u % in_group) / group_rbs;
-    if (rb < 0 || rb >= R || run < 0 || run >= S_grid) fail_now("block order out of range");
-    uint8_t& s = seen[(size_t)rb * S_grid + run];
-    if (s) fail_now("block order visits a tile twice");
-    s = 1;
+    const int sf = s_lo + (u % in_group) / group_rbs * spg;
+    const int sl = std::min(sf + spg, s_hi);
+    if (rb < 0 || rb >= p.R || sf < s_lo || sf >= s_hi) fail_now("block order out of range");
+    for (int sp = sf; sp < sl; ++sp) {
+      uint8_t& v = seen[(size_t)rb * (p.split1 - p.split0) + (sp - p.split0)];
+      if (v) fail_now("block order visits a tile twice");
+      v = 1;
+    }
+    out.push_back(BlockWork{rb, sf, sl});
   }
+  for (uint8_t v : seen)
+    if (!v) fail_now("block order misses a tile");
+  return out;
+}
+
+// (row, split) pairs whose partial the launches of one call wrote; rows are
+// absolute (from the target pointer's offset into the caller's buffer)
+std::vector<uint8_t> g_cover;
+int64_t g_cover_S = 0;
+
+void cover_begin(int64_t N, int64_t S) {
+  g_cover.assign((size_t)(N * S), 0);
+  g_cover_S = S;
+}
+
+void cover_mark(int64_t row, int split) {
+  if (g_cover.empty()) return;
+  uint8_t& v = g_cover[(size_t)(row * g_cover_S + split)];
+  if (v) fail_now("a partial is written by two workgroups");
+  v = 1;
+}
+
+// every row's partials of splits [s0, s1) written exactly once, no other
+void cover_check(const std::string& tag, int s0, int s1) {
+  for (size_t i = 0; i < g_cover.size(); ++i) {
+    const int sp = (int)(i % (size_t)g_cover_S);
+    if (g_cover[i] != (sp >= s0 && sp < s1 ? 1 : 0))
+      fail_now(tag + ": partial coverage differs at row " + std::to_string(i / g_cover_S) +
+               ", split " + std::to_string(sp));
+  }
+  std::fill(g_cover.begin(), g_cover.end(), 0);
 }
 
 }  // namespace
@@ -185,8 +236,11 @@ static void proj_footprint(const ProjParams& p, bool grad) {
   ++g_launches;
   if (p.rows != 128 && p.rows != 256) fail_now("row block height");
   if ((int64_t)p.R != (p.N + p.rows - 1) / p.rows) fail_now("row block count");
-  if ((uint64_t)p.R * p.S_grid * 512 > UINT32_MAX) fail_now("grid exceeds 32-bit work items");
-  check_block_order(p.R, p.S_grid);
+  if ((uint64_t)p.R * (p.runsA + p.split1 - p.splitA) * 512 > UINT32_MAX)
+    fail_now("grid exceeds 32-bit work items");
+  const std::vector<BlockWork> blocks = block_order(p);
+  const int64_t row_base = reinterpret_cast<const int64_t*>(p.target) -
+                           static_cast<const int64_t*>(g_bufs.target.p);
   const uintptr_t H2 = (uintptr_t)p.H * 2;
   touch(reinterpret_cast<uintptr_t>(p.hidden), (size_t)p.N * H2, g_bufs.hidden, false, "hidden");
   touch(reinterpret_cast<uintptr_t>(p.target), (size_t)p.N * 8, g_bufs.target, false, "target");
@@ -209,13 +263,14 @@ static void proj_footprint(const ProjParams& p, bool grad) {
     touch(reinterpret_cast<uintptr_t>(p.g_lse), (size_t)p.N * 4, g_bufs.g_lse, false, "g_lse");
   }
   const int64_t* tgt = p.target;
-  for (int32_t rb = 0; rb < p.R; ++rb) {
-    const int64_t m0 = (int64_t)rb * p.rows;
+  for (const BlockWork& bw : blocks) {
+    const int64_t m0 = (int64_t)bw.rb * p.rows;
     const int rows_here = (int)std::min<int64_t>(p.rows, p.N - m0);
-    for (int32_t run = 0; run < p.S_grid; ++run) {
-      const int split_first = p.split0 + run * p.spg;
-      const int split_last = std::min(split_first + p.spg, p.split1);
-      if (split_first >= p.split1) fail_now("empty split run");
+    if (rows_here < 1) fail_now("a row block without rows");
+    {
+      const int split_first = bw.split_first, split_last = bw.split_last;
+      for (int j = 0; j < rows_here; ++j)
+        for (int sp = split_first; sp < split_last; ++sp) cover_mark(row_base + m0 + j, sp);
       const int vt_begin = split_first * p.vps;
       const int vt_end = std::min(split_last * p.vps, p.T);
       for (int vt = vt_begin; vt < vt_end; ++vt) {
@@ -257,13 +312,15 @@ struct LaunchSeen {
 
 hipError_t launch_proj_lse(const ProjParams& p, hipStream_t) {
   proj_footprint(p, false);
+  const bool tail = p.rows == 128 && p.spg == 1 && p.splitA == p.split1 && g_seen.launches > 0 &&
+                    g_seen.rows == 256;
   if (g_seen.launches++ == 0) {
     g_seen.rows = p.rows;
     g_seen.spg = p.spg;
-  } else if (g_seen.rows != p.rows || g_seen.spg != p.spg) {
+  } else if (!tail && (g_seen.rows != p.rows || g_seen.spg != p.spg)) {
     g_seen.rows = -1;     // row chunks of one call must share the plan
   }
-  g_seen.workgroups += (int64_t)p.R * p.S_grid;
+  g_seen.workgroups += (int64_t)p.R * (p.runsA + p.split1 - p.splitA);
   return hipSuccess;
 }
 
@@ -399,9 +456,13 @@ void forward_case(int64_t N, int64_t H, int64_t V, int bias_dtype, int mode, int
   g_bufs.n_total = N;
   const void* bias = bias_dtype == BILOGP_BIAS_NONE ? nullptr : b.p;
   bilogp::g_seen = bilogp::LaunchSeen{};
+  const int s_mode = N > 0 ? bilogp_num_vocab_splits_mode(N, V, mode, cu) : 0;
+  const int s_inv = bilogp_num_vocab_splits(V);
+  cover_begin(N, s_mode);
   expect(bilogp_forward_mode(h.p, w.p, (const int64_t*)t.p, bias, bias_dtype, (float*)lp.p, (float*)ls.p, N, H,
                              V, mode, cu, ws.p, need, nullptr),
          BILOGP_OK, tag + " forward_mode");
+  cover_check(tag + " forward_mode", 0, s_mode);
   if (N > 0 && cu > 0) {
     // bilogp_launch_plan describes exactly what bilogp_forward_mode launched
     int rows = 0, spg = 0;
@@ -416,23 +477,32 @@ void forward_case(int64_t N, int64_t H, int64_t V, int bias_dtype, int mode, int
                 std::to_string(seen.workgroups) + ")");
   }
   if (mode == BILOGP_SPLITS_INVARIANT) {
+    cover_begin(N, s_inv);
     expect(bilogp_forward_ex(h.p, w.p, (const int64_t*)t.p, bias, bias_dtype, (float*)lp.p, (float*)ls.p, N, H, V,
                              ws.p, need, nullptr),
            BILOGP_OK, tag + " forward_ex");
+    cover_check(tag + " forward_ex", 0, s_inv);
     expect(bilogp_partials(h.p, w.p, (const int64_t*)t.p, bias, bias_dtype, N, H, V, ws.p, need, nullptr),
            BILOGP_OK, tag + " partials");
+    cover_check(tag + " partials", 0, s_inv);
     expect(bilogp_merge((const int64_t*)t.p, ws.p, need, (float*)lp.p, (float*)ls.p, N, V, nullptr),
            BILOGP_OK, tag + " merge");
+    cover_check(tag + " merge", 0, 0);
     g_bufs.ws = Span{};   // library-owned workspaces from here on
-    if (bias_dtype != BILOGP_BIAS_BF16)
+    if (bias_dtype != BILOGP_BIAS_BF16) {
       expect(bilogp_forward(h.p, w.p, (const int64_t*)t.p, (const float*)bias, (float*)lp.p,
                             (float*)ls.p, N, H, V, nullptr),
              BILOGP_OK, tag + " forward");
-    if (need <= bilogp_noalloc_max_workspace_bytes())
+      cover_check(tag + " forward", 0, s_inv);
+    }
+    if (need <= bilogp_noalloc_max_workspace_bytes()) {
       expect(bilogp_forward_noalloc(h.p, w.p, (const int64_t*)t.p, bias, bias_dtype, (float*)lp.p,
                                     (float*)ls.p, N, H, V, nullptr),
              BILOGP_OK, tag + " forward_noalloc");
+      cover_check(tag + " forward_noalloc", 0, s_inv);
+    }
   }
+  g_cover.clear();
 }
 
 // Vocabulary-range partials from an exact-size weight (and bias) slice.
@@ -454,10 +524,13 @@ void range_case(int64_t N, int64_t H, int64_t V, int s0, int s1, int bias_dtype)
   g_bufs.bias = b.span();
   g_bufs.ws = ws.span();
   g_bufs.n_total = N;
+  cover_begin(N, bilogp_num_vocab_splits(V));
   expect(bilogp_partials_range(h.p, w.p, (const int64_t*)t.p,
                                bias_dtype == BILOGP_BIAS_NONE ? nullptr : b.p, bias_dtype, N, H,
                                V, s0, s1, ws.p, need, nullptr),
          BILOGP_OK, tag);
+  cover_check(tag, s0, s1);
+  g_cover.clear();
 }
 
 void backward_case(int64_t N, int64_t H, int64_t V, int bias_dtype, bool with_gb) {
@@ -482,12 +555,15 @@ void backward_case(int64_t N, int64_t H, int64_t V, int bias_dtype, bool with_gb
   g_bufs.g_lse = gs.span();
   g_bufs.gb = gb.span();
   g_bufs.ws = ws.span();
+  cover_begin(N, bilogp_num_vocab_splits(V));
   expect(bilogp_backward(h.p, w.p, (const int64_t*)t.p,
                          bias_dtype == BILOGP_BIAS_NONE ? nullptr : b.p, bias_dtype,
                          (const float*)l.p, (const float*)gl.p, (const float*)gs.p, (float*)gh.p,
                          (float*)gw.p, with_gb ? (float*)gb.p : nullptr, N, H, V, ws.p, need,
                          nullptr),
          BILOGP_OK, tag);
+  cover_check(tag, 0, bilogp_num_vocab_splits(V));
+  g_cover.clear();
 }
 
 void gemm_case(int64_t M, int64_t N, int64_t K, int kind) {
@@ -506,25 +582,32 @@ void gemm_case(int64_t M, int64_t N, int64_t K, int kind) {
 }  // namespace
 
 int main() {
-  // forward, all split modes and launch plans (few / many compute units)
-  for (int cu : {1, 80, 256, 1024}) {
-    g_cu_count = cu;
-    forward_case(8, 64, 1000, BILOGP_BIAS_NONE, BILOGP_SPLITS_INVARIANT, 0);
-    forward_case(300, 200, 2000, BILOGP_BIAS_F32, BILOGP_SPLITS_INVARIANT, 0);
-    forward_case(513, 64, 257, BILOGP_BIAS_BF16, BILOGP_SPLITS_INVARIANT, cu);
-    forward_case(1, 16, 128256, BILOGP_BIAS_NONE, BILOGP_SPLITS_INVARIANT, 0);
-    forward_case(4096, 8, 151936, BILOGP_BIAS_BF16, BILOGP_SPLITS_INVARIANT, 0);
-    forward_case(777, 8, 70001, BILOGP_BIAS_F32, BILOGP_SPLITS_THROUGHPUT, cu);
-    forward_case(37, 16, 128256, BILOGP_BIAS_NONE, BILOGP_SPLITS_THROUGHPUT, cu);
-    forward_case(5, 8, 1, BILOGP_BIAS_NONE, BILOGP_SPLITS_INVARIANT, 0);
-  }
+  // The library reads the device's compute-unit count once, at its first
+  // call: 256 here.  Other counts reach the plans through forward_mode's
+  // explicit count (forward_ex and the rest schedule for the device's).
   g_cu_count = 256;
   forward_case(0, 64, 1000, BILOGP_BIAS_NONE, BILOGP_SPLITS_INVARIANT, 0);
+  // forward, all split modes and launch plans (few / many compute units)
+  for (int cu : {1, 80, 256, 1024}) {
+    forward_case(8, 64, 1000, BILOGP_BIAS_NONE, BILOGP_SPLITS_INVARIANT, cu);
+    forward_case(300, 200, 2000, BILOGP_BIAS_F32, BILOGP_SPLITS_INVARIANT, cu);
+    forward_case(513, 64, 257, BILOGP_BIAS_BF16, BILOGP_SPLITS_INVARIANT, cu);
+    forward_case(1, 16, 128256, BILOGP_BIAS_NONE, BILOGP_SPLITS_INVARIANT, cu);
+    forward_case(4096, 8, 151936, BILOGP_BIAS_BF16, BILOGP_SPLITS_INVARIANT, cu);
+    forward_case(777, 8, 70001, BILOGP_BIAS_F32, BILOGP_SPLITS_THROUGHPUT, cu);
+    forward_case(37, 16, 128256, BILOGP_BIAS_NONE, BILOGP_SPLITS_THROUGHPUT, cu);
+    forward_case(5, 8, 1, BILOGP_BIAS_NONE, BILOGP_SPLITS_INVARIANT, cu);
+  }
   // vocabulary ranges: exact-size weight and bias slices (the shifted base)
   for (auto r : std::vector<std::pair<int, int>>{{0, 1}, {0, 251}, {7, 9}, {250, 251}, {100, 200}})
     for (int bd : {BILOGP_BIAS_NONE, BILOGP_BIAS_BF16, BILOGP_BIAS_F32})
       range_case(300, 16, 128256, r.first, r.second, bd);
   range_case(1, 8, 16385, 32, 33, BILOGP_BIAS_F32);
+  // split schedules with a second, 128-token launch (whole rounds of the big
+  // launch, the remainder as half-height pieces), forward and backward
+  forward_case(4000, 1024, 50257, BILOGP_BIAS_F32, BILOGP_SPLITS_INVARIANT, 256);
+  forward_case(4000, 1024, 50257, BILOGP_BIAS_NONE, BILOGP_SPLITS_INVARIANT, 80);
+  backward_case(1024, 1024, 20480, BILOGP_BIAS_BF16, true);
   // backward (the softmax-gradient footprint, padding, row sums)
   backward_case(7, 16, 1000, BILOGP_BIAS_NONE, false);
   backward_case(300, 8, 2003, BILOGP_BIAS_BF16, true);

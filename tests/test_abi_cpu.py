@@ -37,13 +37,14 @@ def test_library_exports_every_declared_symbol():
 
 def test_constants_and_version():
     # ABI 2 added bilogp_bit_contract_version and the scheduling compute-unit
-    # count of the invariant mode; ABI 3 added H to bilogp_launch_plan.  Bit contract 2: tiles of 256 columns, at
+    # count of the invariant mode; ABI 3 added H to bilogp_launch_plan; ABI 4
+    # added bilogp_launch_schedule.  Bit contract 2: tiles of 256 columns, at
     # most 256 splits, the merge tree over consecutive per-lane split blocks
     # (contract 1 had at most 64 splits and lane-strided pre-sums).  Bit
     # contract 3: K in 32-wide steps of the 16 x 16 x 32 bf16 MFMA, per-token
     # sums over (lane group, register) of that tile layout.  Bit contract 4:
     # the deterministic GEMM and the backward's products on that MFMA too.
-    assert ila.bilogp_abi_version() == 3
+    assert ila.bilogp_abi_version() == 4
     assert ila.bilogp_bit_contract_version() == 4
     assert ila.bilogp_vtile_cols() == 256
     assert ila.bilogp_max_splits() == 256
@@ -561,7 +562,10 @@ def test_launch_plan_follows_the_compute_units_only_in_scheduling():
         plans = {cu: ila.bilogp_launch_plan(n, 4096, V, inv, cu) for cu in cus}
         for cu, (rows, spg, wgs) in plans.items():
             assert rows in (128, 256) and spg >= 1
-            assert wgs == -(-n // rows) * -(-198 // spg)
+            sa, st = ila.bilogp_launch_schedule(n, 4096, V, inv, cu)
+            assert 0 <= sa <= st <= 198 and sa % spg == 0
+            assert wgs == (-(-n // rows) * (-(-sa // spg) + st - sa)
+                           + (-(-n // 128) * (198 - st) if st < 198 else 0))
         # few compute units: 256-token blocks; enough of them: 128-token blocks
         assert plans[1][0] == 256 and plans[65536][0] == 128
         assert len(set(plans.values())) >= 2
@@ -602,7 +606,13 @@ def _plan_model(N, H, V, cu):
     workgroup per compute unit (ties to the longer run); 128-token row blocks only
     when 256-token blocks leave units idle and the 128-token plan's K stages per
     unit, at 15/32 of a 256-token stage, come out fewer (stages per tile rounded up
-    to 2 buffers for 256-token blocks, 3 for 128-token blocks)."""
+    to 2 buffers for 256-token blocks, 3 for 128-token blocks).  With 256-token
+    blocks, a split schedule: the last ts splits (2 R ts <= cu) to a 128-token
+    launch, the rest in whole rounds where they fit, single splits for the last
+    ceil(3 cu / R) of them per row block, where the cost in 256-token stages per
+    unit (x 32: 32 per 256-token stage and per workgroup start, 19 per 128-token
+    stage, 3 stages for the second launch) beats the one-launch plan's.
+    Returns (rows, spg, workgroups, split_a, split_t)."""
     T = -(-V // 256)
     vps = -(-T // 256)
     S = -(-T // vps)
@@ -629,7 +639,25 @@ def _plan_model(N, H, V, cu):
         rows = 128 if c128 * 15 < c256 * 32 else 256
     R = -(-N // rows)
     g = spr(R)
-    return rows, g, R * -(-S // g)
+    sa = st = S
+    if rows == 256 and R * S > cu and R * S <= (2 ** 32 - 1) // 512:
+        k = -(-H // 64)
+        kt256, kt128 = -(-k // 2) * 2, -(-k // 3) * 3
+        wgs = R * -(-S // g)
+        best = 32 * (-(-wgs // cu) * g * vps * kt256 + -(-wgs // cu))
+        cap = min(max(1, 4 // vps), S)
+        b_min = -(-3 * cu // R)
+        ts = 1
+        while ts < S and 2 * R * ts <= cu:
+            sb = S - ts
+            a = max(0, sb - b_min) // cap * cap
+            starts = -(-(R * (a // cap)) // cu) + -(-(R * (sb - a)) // cu) + 1
+            cost = 32 * (-(-(R * sb) // cu) * vps * kt256 + starts + 3) + 19 * vps * kt128
+            if cost < best:
+                best, g, sa, st = cost, (cap if a > 0 else 1), a, sb
+            ts += 1
+    wgs = R * (-(-sa // g) + st - sa) + (-(-N // 128) * (S - st) if st < S else 0)
+    return rows, g, wgs, sa, st
 
 
 def test_launch_plan_matches_its_stated_rules():
@@ -641,4 +669,6 @@ def test_launch_plan_matches_its_stated_rules():
         H = int(rng.integers(1, 8193)) * 8
         V = int(rng.choice([rng.integers(1, 5000), rng.integers(1, 300000), rng.integers(1, 1 << 30)]))
         cu = int(rng.choice([rng.integers(1, 64), 80, 256, 304, rng.integers(1, 4096)]))
-        assert ila.bilogp_launch_plan(N, H, V, inv, cu) == _plan_model(N, H, V, cu), (N, H, V, cu)
+        model = _plan_model(N, H, V, cu)
+        assert ila.bilogp_launch_plan(N, H, V, inv, cu) == model[:3], (N, H, V, cu)
+        assert ila.bilogp_launch_schedule(N, H, V, inv, cu) == model[3:], (N, H, V, cu)

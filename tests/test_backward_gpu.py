@@ -205,6 +205,32 @@ def test_grad_hidden_rows_do_not_depend_on_the_batch(N, H, V, chunk):
     assert torch.equal(permuted, full[perm])
 
 
+def test_split_schedule_with_a_second_launch_keeps_the_bits():
+    """N = 1024, H = 1024, V = 20480 on 256 compute units: 4 row blocks x 80
+    splits, scheduled as one round of 256 whole tiles plus the last 16 splits
+    as 128 half-height pieces in a second launch.  256-row chunks run
+    128-token blocks in one launch.  dZ^T (the workspace) and grad_hidden of
+    every row are the same bits either way."""
+    N, H, V = 1024, 1024, 20480
+    S = ila.bilogp_num_vocab_splits(V)
+    if ila.device_cu_count(DEV) == 256:
+        assert ila.bilogp_launch_schedule(N, H, V, ila.BILOGP_SPLITS_INVARIANT, 256)[1] < S
+    inp, up = _inputs(N, H, V, 9, "bf16")
+    say(f"backward split schedule N={N} H={H} V={V}")
+    with torch.no_grad():
+        _, lse = ila.forward(inp["hidden"], inp["weight"], inp["target"], inp["bias"])
+    full, _, _, ws = _run(inp, up, lse)
+    full_dz = _dzt(ws, N, V).clone()
+    for i in range(0, N, 256):
+        sl = slice(i, i + 256)
+        sub = {k: (v[sl] if k in ("hidden", "target") else v) for k, v in inp.items()}
+        sup = {k: v[sl] for k, v in up.items()}
+        gh, _, _, wsc = _run(sub, sup, lse[sl])
+        torch.cuda.synchronize()
+        assert torch.equal(gh, full[sl]), f"grad_hidden rows {i}.. differ"
+        assert torch.equal(_dzt(wsc, 256, V), full_dz[:, sl]), f"dZ rows {i}.. differ"
+
+
 def test_run_to_run_and_streams():
     """Every output, on a second call and on a side stream, is the same bits."""
     N, H, V = 600, 384, 1500

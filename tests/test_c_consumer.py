@@ -70,7 +70,7 @@ def test_c_program_calls_the_library(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120, env=env)
     assert r.returncode == 0, r.stderr
     lines = r.stdout.splitlines()
-    assert lines[0] == "abi 3 contract 4"
+    assert lines[0] == "abi 4 contract 4"
     assert lines[1] == "splits 251 vps 2"
     # [N, S] (max, sum) pairs + [N] target logits + the padded fp32 bias, 256-byte parts
     assert lines[2] == f"ws {4096 * 251 * 8 + 4096 * 4 + 128256 * 4}"

@@ -73,8 +73,15 @@ MUTATIONS = {
                                     "q.part = p.part + (r0 + 1) * p.S;"),
     # a launch plan that counts the 128-token stages with two buffers instead of
     # the three the forward launches with
-    "launch_plan_wrong_buffer_count": ("  const int32_t rows = row_block_rows(N, H, S, vps, cu_count, 3);",
-                                       "  const int32_t rows = row_block_rows(N, H, S, vps, cu_count, 2);"),
+    "launch_plan_wrong_buffer_count": ("  plan_projection(p, cu_count, 3);",
+                                       "  plan_projection(p, cu_count, 2);"),
+    # a split schedule whose big launch also runs the splits of the second launch
+    "main_launch_overlaps_tail": ("  q.split1 = p.splitT;\n", "  q.split1 = p.split1;\n"),
+    # a second launch that starts one split late
+    "tail_launch_skips_a_split": ("  q.split0 = p.splitT;\n", "  q.split0 = p.splitT + 1;\n"),
+    # a second launch sized from 256-token row blocks (its last rows never run)
+    "tail_launch_too_few_row_blocks": ("  q.R = (int32_t)((p.N + 127) / 128);",
+                                       "  q.R = (int32_t)((p.N + 255) / 256);"),
 }
 
 

@@ -7,6 +7,8 @@ annotation on the chunk test: full-batch bits equal concatenated chunk bits.
 The sweep workload's full batch runs 256-token row blocks and its chunks of up
 to 1000 rows 128-token blocks (too few 256-token blocks to fill the device),
 so the chunk comparison also holds the two block heights to the same bits.
+On 256 compute units the full batch's schedule also has a second launch: 12
+whole rounds of 256-token tiles, and the last 6 splits as 128-token pieces.
 """
 
 import pytest
@@ -35,6 +37,10 @@ def test_chunked_equals_full(chunk):
     inp, full_lp, full_ls = sweep_inputs()
     h, t = flat(inp)
     N = h.shape[0]
+    V = inp["weight"].shape[0]
+    if ila.device_cu_count(DEV) == 256:
+        sa, st = ila.bilogp_launch_schedule(N, h.shape[1], V, ila.BILOGP_SPLITS_INVARIANT, 256)
+        assert st < ila.bilogp_num_vocab_splits(V), "the full batch has no second launch"
     say(f"sweep chunk={chunk}")
     lps, lss = [], []
     for c0 in range(0, N, chunk):
