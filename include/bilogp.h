@@ -133,7 +133,9 @@ int bilogp_num_vocab_splits(int64_t V);
 /* Bytes of device workspace bilogp_forward_ex needs for N rows and vocabulary
  * size V: the [N, S] partial (max, sum-exp) pairs, the [N] target logits and
  * an fp32 copy of the bias padded to whole 256-column tiles (reserved whether
- * or not a call passes a bias), each 256-byte aligned.  0 for N == 0;
+ * or not a call passes a bias; used only for a bias that cannot be read in
+ * place, i.e. one not 16-byte aligned or whose V is not a multiple of 4 (fp32)
+ * or 8 (bf16)), each 256-byte aligned.  0 for N == 0;
  * (size_t)-1 for invalid N or V. */
 size_t bilogp_workspace_bytes(int64_t N, int64_t V);
 

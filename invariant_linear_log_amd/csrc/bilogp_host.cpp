@@ -194,6 +194,43 @@ Schedule schedule_256(int64_t R, int ns, int vps, int cu, int64_t kt256, int64_t
 
 int device_cus(int dev) { return g_cu_count[dev].load(std::memory_order_acquire); }
 
+// Whether the projection reads the caller's bias directly: 16-byte aligned
+// and V a whole number of 16-byte chunks of it, so that the kernel's
+// per-tile descriptor (the tile's columns below V) never cuts a chunk.
+// Otherwise the host first writes a zero-padded fp32 copy into the
+// workspace.  Either way the kernel adds the same fp32 value.
+bool bias_direct(int bias_dtype, int64_t V, const void* bias) {
+  if (!bias || reinterpret_cast<uintptr_t>(bias) % 16 != 0) return false;
+  if (bias_dtype == BILOGP_BIAS_F32) return V % 4 == 0;
+  if (bias_dtype == BILOGP_BIAS_BF16) return V % 8 == 0;
+  return false;
+}
+
+// The kernel's view of a bias: its source kind and base address, shifted back
+// by col0 columns (absolute-column addressing), reading the caller's values
+// where bias_direct allows, else the fp32 copy at bias32.
+void set_bias(bilogp::ProjParams& p, const void* bias, int bias_dtype, int64_t V, int64_t col0,
+              float* bias32) {
+  p.bias_kind = bias_dtype == BILOGP_BIAS_BF16 ? bilogp::kBiasBf16
+                : bias_dtype == BILOGP_BIAS_F32 ? bilogp::kBiasF32
+                                                : bilogp::kBiasNone;
+  if (!bias) {
+    p.bias = nullptr;
+    p.bias_src = bilogp::kBiasSrcNone;
+    p.bias_copy = 0;
+  } else if (bias_direct(bias_dtype, V, bias)) {
+    const uintptr_t esz = bias_dtype == BILOGP_BIAS_F32 ? 4 : 2;
+    p.bias = reinterpret_cast<const void*>(reinterpret_cast<uintptr_t>(bias) - (uintptr_t)col0 * esz);
+    p.bias_src = bias_dtype == BILOGP_BIAS_F32 ? bilogp::kBiasSrcF32 : bilogp::kBiasSrcBf16;
+    p.bias_copy = 0;
+  } else {
+    p.bias = reinterpret_cast<const void*>(reinterpret_cast<uintptr_t>(bias32) -
+                                           (uintptr_t)col0 * sizeof(float));
+    p.bias_src = bilogp::kBiasSrcF32;
+    p.bias_copy = 1;
+  }
+}
+
 // Workgroups a launch may have (the grid stays within 32-bit work-item
 // counts); a call with more row blocks x splits keeps the one-phase schedule
 // and is issued in row chunks.
@@ -493,17 +530,12 @@ bilogp_status validate(const Call& c, int parts, bilogp::ProjParams* out) {
   p.weight = reinterpret_cast<const void*>(reinterpret_cast<uintptr_t>(c.weight) -
                                            (uintptr_t)col0 * (uintptr_t)c.H * 2u);
   p.target = c.target;
-  p.bias = c.bias ? reinterpret_cast<const float*>(reinterpret_cast<uintptr_t>(L.bias32) -
-                                                    (uintptr_t)col0 * sizeof(float))
-                  : nullptr;   // the kernel reads the padded fp32 copy
+  set_bias(p, c.bias, c.bias_dtype, c.V, col0, L.bias32);
   p.part = L.part;
   p.tlogit = L.tlogit;
   p.N = c.N;
   p.H = (int32_t)c.H;
   p.V = (int32_t)c.V;
-  p.bias_kind = c.bias_dtype == BILOGP_BIAS_BF16 ? bilogp::kBiasBf16
-                : c.bias_dtype == BILOGP_BIAS_F32 ? bilogp::kBiasF32
-                                                  : bilogp::kBiasNone;
   p.T = (int32_t)((c.V + bilogp::kVtileCols - 1) / bilogp::kVtileCols);
   p.vps = vps;
   p.S = S;
@@ -527,7 +559,7 @@ constexpr int64_t kMergeChunkRows = int64_t(1) << 25;
 
 bilogp_status launch(const bilogp::ProjParams& p, const Call& c, int parts, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((parts & kProj) && c.bias) {
+  if ((parts & kProj) && p.bias_copy) {
     // the padded fp32 copy of the bias columns the launch reads, from col0
     const int64_t cols = c.split_end >= 0
         ? std::min<int64_t>((int64_t)p.split1 * p.vps * bilogp::kVtileCols, p.V) -
@@ -943,18 +975,17 @@ bilogp_status bilogp_backward(const void* hidden, const void* weight, const int6
                                                        : bilogp::kBiasNone;
   hipError_t e = hipSuccess;
   if (N > 0) {
-    if (bias) e = bilogp::launch_bias_f32(bias, kind, (int32_t)V, bias32, s);
+    bilogp::ProjParams p{};
+    set_bias(p, bias, bias_dtype, V, 0, bias32);
+    if (p.bias_copy) e = bilogp::launch_bias_f32(bias, kind, (int32_t)V, bias32, s);
     if (e == hipSuccess) e = bilogp::launch_zero_pad_cols(dzt, V, N, ldz, s);
     if (e == hipSuccess) {
-      bilogp::ProjParams p{};
       p.hidden = hidden;
       p.weight = weight;
       p.target = target;
-      p.bias = bias ? bias32 : nullptr;
       p.N = N;
       p.H = (int32_t)H;
       p.V = (int32_t)V;
-      p.bias_kind = kind;
       p.T = (int32_t)((V + bilogp::kVtileCols - 1) / bilogp::kVtileCols);
       p.vps = bilogp_vtiles_per_split(V);
       p.S = bilogp_num_vocab_splits(V);

@@ -20,17 +20,24 @@ constexpr int kBlockRows = 256;
 
 enum BiasKind : int32_t { kBiasNone = 0, kBiasBf16 = 1, kBiasF32 = 2 };
 
+// What the projection kernels read at ProjParams::bias: fp32 values (the
+// caller's fp32 bias, or a zero-padded fp32 copy of any bias) or the caller's
+// bf16 values.
+enum BiasSrc : int32_t { kBiasSrcNone = 0, kBiasSrcF32 = 1, kBiasSrcBf16 = 2 };
+
 struct ProjParams {
   const void* hidden;      // bf16 [N, H], row-major
   const void* weight;      // bf16 [V, H], row-major
   const int64_t* target;   // [N]
-  const void* bias;        // fp32 [ceil(V / kVtileCols) * kVtileCols] or null
+  const void* bias;        // read as bias_src says, addressed by absolute column; or null
   float2* part;            // [N, S]: per (row, split) running max and sum of exp(z - max)
   float* tlogit;           // [N]: logit of each row's target
   int64_t N;
   int32_t H;
   int32_t V;
-  int32_t bias_kind;
+  int32_t bias_kind;       // the caller's bias dtype (BiasKind)
+  int32_t bias_src;        // BiasSrc
+  int32_t bias_copy;       // host only: bias is the fp32 copy, filled before the launch
   int32_t T;               // vocabulary tiles, ceil(V / kVtileCols)
   int32_t vps;             // tiles per split
   int32_t S;               // splits

@@ -139,15 +139,17 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
-// The kernel body.  kTj token blocks of 16 per wave: 4 (256-token row
-// blocks) or 2 (128-token row blocks, for batches too small to give every
-// compute unit a 256-token block); kSlots LDS buffers.  With kGrad it is the
+// The kernel body.  kBias: no bias (0), or the bias read as fp32 (1) or as
+// bf16 (2) values, widened on reading.  kTj token blocks of 16 per wave: 4
+// (256-token row blocks) or 2 (128-token row blocks, for batches too small to
+// give every compute unit a 256-token block); kSlots LDS buffers.  With kGrad it is the
 // softmax-gradient pass of the backward: the same tiles and the same
 // accumulation (z has the forward's bits), and a tile epilogue that writes
 // dZ = p (g_lse - g_logp) + g_logp [v == target], p = exp(z - lse), instead
 // of reducing it.
-template <bool kHasBias, bool kGrad, int kTj, int kSlots>
+template <int kBias, bool kGrad, int kTj, int kSlots>
 __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
+  constexpr bool kHasBias = kBias != 0;
   static_assert(kTj == 4 || kTj == 2, "two or four 16-token blocks per wave");
   static_assert(kSlots == 2 || (kSlots == 3 && kTj == 2), "three buffers fit 128-token blocks");
   constexpr int kRows = 64 * kTj;                  // tokens per row block
@@ -348,8 +350,12 @@ __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
     floatx4 acc[8][kTj];
 
     // The bias of tile v reaches LDS (bias_lds[v & 1]) by one direct load of
-    // 1 KB from wave 0, issued in the epilogue of tile v - 1 once that tile's
-    // bias is consumed (tile 0: in the prologue).  A stage barrier of tile v
+    // 1 KB (fp32) or 512 bytes (bf16, lanes 0-31) from wave 0, issued in the
+    // epilogue of tile v - 1 once that tile's bias is consumed (tile 0: in the
+    // prologue).  The descriptor covers the tile's columns below V; the host
+    // takes this path only where V keeps every 16-byte chunk wholly inside
+    // or wholly past it (chunks past V read as zero), else it passes a
+    // zero-padded fp32 copy.  A stage barrier of tile v
     // makes it visible: the first one with two buffers (it waits for every
     // load); with three, where a barrier leaves the newest six loads in
     // flight, the first one after six more loads - one or two stages on, long
@@ -359,11 +365,15 @@ __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
     auto load_bias = [&](int v) {
       if constexpr (kHasBias) {
         if (wave == 0 && v < nvt) {
+          constexpr int kEsz = kBias == 2 ? 2 : 4;
+          const int vb = (vt_begin + v) * kVtileCols;
           const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-              (void*)((const float*)p.bias + (int64_t)(vt_begin + v) * kVtileCols), (short)0,
-              kVtileCols * 4, kRsrcWord3);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)&bias_lds[v & 1][0], 16,
-                                                   (uint32_t)lane * 16u, 0, 0, 0);
+              (void*)((const uint8_t*)p.bias + (int64_t)vb * kEsz), (short)0,
+              min(kVtileCols, p.V - vb) * kEsz, kRsrcWord3);
+          const uint32_t off =
+              (kEsz == 4 || lane < 32) ? (uint32_t)lane * 16u : kOutOfRange;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)&bias_lds[v & 1][0], 16, off,
+                                                   0, 0, 0);
         }
       }
     };
@@ -575,10 +585,19 @@ __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
       if constexpr (kHasBias) {
         // z = (the K accumulation) + bias: one fp32 add per logit
         __builtin_amdgcn_sched_barrier(0);
-        const float* bt = &bias_lds[v & 1][wv * 128 + 4 * lg];
+        const int bcol = wv * 128 + 4 * lg;         // + 16 vi: this lane's four columns
 #pragma unroll
         for (int vi = 0; vi < 8; ++vi) {
-          const floatx4 bb = *(const floatx4*)(bt + vi * 16);
+          floatx4 bb;
+          if constexpr (kBias == 2) {
+            // four bf16 values; bf16 -> fp32 is the bits shifted up 16 (exact)
+            const uint2 raw =
+                *(const uint2*)((const uint16_t*)&bias_lds[v & 1][0] + bcol + vi * 16);
+            bb = floatx4{__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xffff0000u),
+                         __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xffff0000u)};
+          } else {
+            bb = *(const floatx4*)(&bias_lds[v & 1][bcol + vi * 16]);
+          }
 #pragma unroll
           for (int e = 0; e < 4; ++e)
 #pragma unroll
@@ -706,30 +725,42 @@ __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
 }
 
 __global__ __launch_bounds__(kThreads, 1) void proj_lse_kernel(const ProjParams p) {
-  proj_fwd_body<false, false, 4, 2>(p);
+  proj_fwd_body<0, false, 4, 2>(p);
 }
 __global__ __launch_bounds__(kThreads, 1) void proj_lse_bias_kernel(const ProjParams p) {
-  proj_fwd_body<true, false, 4, 2>(p);
+  proj_fwd_body<1, false, 4, 2>(p);
+}
+__global__ __launch_bounds__(kThreads, 1) void proj_lse_bias16_kernel(const ProjParams p) {
+  proj_fwd_body<2, false, 4, 2>(p);
 }
 __global__ __launch_bounds__(kThreads, 1) void softmax_grad_kernel(const ProjParams p) {
-  proj_fwd_body<false, true, 4, 2>(p);
+  proj_fwd_body<0, true, 4, 2>(p);
 }
 __global__ __launch_bounds__(kThreads, 1) void softmax_grad_bias_kernel(const ProjParams p) {
-  proj_fwd_body<true, true, 4, 2>(p);
+  proj_fwd_body<1, true, 4, 2>(p);
+}
+__global__ __launch_bounds__(kThreads, 1) void softmax_grad_bias16_kernel(const ProjParams p) {
+  proj_fwd_body<2, true, 4, 2>(p);
 }
 // 128-token row blocks: twice the workgroups for batches that 256-token
 // blocks cannot spread over every compute unit; the same bits
 __global__ __launch_bounds__(kThreads, 1) void proj_lse_r128_kernel(const ProjParams p) {
-  proj_fwd_body<false, false, 2, 3>(p);
+  proj_fwd_body<0, false, 2, 3>(p);
 }
 __global__ __launch_bounds__(kThreads, 1) void proj_lse_bias_r128_kernel(const ProjParams p) {
-  proj_fwd_body<true, false, 2, 3>(p);
+  proj_fwd_body<1, false, 2, 3>(p);
+}
+__global__ __launch_bounds__(kThreads, 1) void proj_lse_bias16_r128_kernel(const ProjParams p) {
+  proj_fwd_body<2, false, 2, 3>(p);
 }
 __global__ __launch_bounds__(kThreads, 1) void softmax_grad_r128_kernel(const ProjParams p) {
-  proj_fwd_body<false, true, 2, 3>(p);
+  proj_fwd_body<0, true, 2, 3>(p);
 }
 __global__ __launch_bounds__(kThreads, 1) void softmax_grad_bias_r128_kernel(const ProjParams p) {
-  proj_fwd_body<true, true, 2, 3>(p);
+  proj_fwd_body<1, true, 2, 3>(p);
+}
+__global__ __launch_bounds__(kThreads, 1) void softmax_grad_bias16_r128_kernel(const ProjParams p) {
+  proj_fwd_body<2, true, 2, 3>(p);
 }
 
 }  // namespace
@@ -737,9 +768,12 @@ __global__ __launch_bounds__(kThreads, 1) void softmax_grad_bias_r128_kernel(con
 hipError_t launch_softmax_grad(const ProjParams& p, hipStream_t stream) {
   const int64_t blocks = (int64_t)p.R * (p.runsA + p.split1 - p.splitA);
   if (blocks <= 0) return hipSuccess;
-  const bool bias = p.bias_kind != kBiasNone;
-  auto k = p.rows == 128 ? (bias ? softmax_grad_bias_r128_kernel : softmax_grad_r128_kernel)
-                         : (bias ? softmax_grad_bias_kernel : softmax_grad_kernel);
+  auto k = p.rows == 128 ? (p.bias_src == kBiasSrcBf16  ? softmax_grad_bias16_r128_kernel
+                           : p.bias_src == kBiasSrcF32 ? softmax_grad_bias_r128_kernel
+                                                       : softmax_grad_r128_kernel)
+                         : (p.bias_src == kBiasSrcBf16  ? softmax_grad_bias16_kernel
+                           : p.bias_src == kBiasSrcF32 ? softmax_grad_bias_kernel
+                                                       : softmax_grad_kernel);
   hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
@@ -747,9 +781,12 @@ hipError_t launch_softmax_grad(const ProjParams& p, hipStream_t stream) {
 hipError_t launch_proj_lse(const ProjParams& p, hipStream_t stream) {
   const int64_t blocks = (int64_t)p.R * (p.runsA + p.split1 - p.splitA);
   if (blocks <= 0) return hipSuccess;
-  const bool bias = p.bias_kind != kBiasNone;
-  auto k = p.rows == 128 ? (bias ? proj_lse_bias_r128_kernel : proj_lse_r128_kernel)
-                         : (bias ? proj_lse_bias_kernel : proj_lse_kernel);
+  auto k = p.rows == 128 ? (p.bias_src == kBiasSrcBf16  ? proj_lse_bias16_r128_kernel
+                           : p.bias_src == kBiasSrcF32 ? proj_lse_bias_r128_kernel
+                                                       : proj_lse_r128_kernel)
+                         : (p.bias_src == kBiasSrcBf16  ? proj_lse_bias16_kernel
+                           : p.bias_src == kBiasSrcF32 ? proj_lse_bias_kernel
+                                                       : proj_lse_kernel);
   hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }

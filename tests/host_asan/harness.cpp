@@ -254,9 +254,20 @@ static void proj_footprint(const ProjParams& p, bool grad) {
     tl_span = Span{static_cast<const uint8_t*>(g_bufs.ws.p) + (pb + 255) / 256 * 256,
                    (size_t)g_bufs.n_total * 4};
   }
-  const Span b32_span = p.bias ? ws_span_for(reinterpret_cast<const void*>(
-                                     reinterpret_cast<uintptr_t>(p.bias) + (uintptr_t)p.col0 * 4))
-                               : Span{};
+  // the kernel reads the caller's bias (fp32 or bf16) or the fp32 copy in the
+  // workspace; either way from col0 on, addressed by absolute column
+  const uintptr_t besz = p.bias_src == kBiasSrcBf16 ? 2 : 4;
+  if ((p.bias != nullptr) != (p.bias_src != kBiasSrcNone)) fail_now("bias source");
+  if (p.bias_copy && p.bias_src != kBiasSrcF32) fail_now("the bias copy is fp32");
+  const Span b_span = !p.bias ? Span{}
+                      : p.bias_copy ? ws_span_for(reinterpret_cast<const void*>(
+                                          reinterpret_cast<uintptr_t>(p.bias) + p.col0 * besz))
+                                    : g_bufs.bias;
+  if (p.bias && !p.bias_copy &&
+      (reinterpret_cast<uintptr_t>(p.bias) + p.col0 * besz) % 16 != 0)
+    fail_now("a direct bias read from a base that is not 16-byte aligned");
+  if (p.bias && !p.bias_copy && (p.V * besz) % 16 != 0)
+    fail_now("a direct bias read whose last 16-byte chunk is cut by V");
   if (grad) {
     touch(reinterpret_cast<uintptr_t>(p.lse), (size_t)p.N * 4, g_bufs.lse_in, false, "lse");
     touch(reinterpret_cast<uintptr_t>(p.g_logp), (size_t)p.N * 4, g_bufs.g_logp, false, "g_logp");
@@ -280,8 +291,8 @@ static void proj_footprint(const ProjParams& p, bool grad) {
         touch(reinterpret_cast<uintptr_t>(p.weight) + (uintptr_t)vbase * H2, (size_t)vrows * H2,
               g_bufs.weight, false, "weight");
         if (p.bias)
-          touch(reinterpret_cast<uintptr_t>(p.bias) + (uintptr_t)vbase * 4, kVtileCols * 4,
-                b32_span, false, "bias copy (read)");
+          touch(reinterpret_cast<uintptr_t>(p.bias) + (uintptr_t)vbase * besz,
+                (size_t)vrows * besz, b_span, false, p.bias_copy ? "bias copy (read)" : "bias");
         if (grad)
           for (int j = 0; j < rows_here; ++j)
             for (int c = 0; c < vrows; ++c)
@@ -605,6 +616,9 @@ int main() {
   range_case(1, 8, 16385, 32, 33, BILOGP_BIAS_F32);
   // split schedules with a second, 128-token launch (whole rounds of the big
   // launch, the remainder as half-height pieces), forward and backward
+  // bias read directly (V a whole number of 16-byte chunks) or through the copy
+  forward_case(40, 16, 1004, BILOGP_BIAS_BF16, BILOGP_SPLITS_INVARIANT, 256);
+  forward_case(40, 16, 1004, BILOGP_BIAS_F32, BILOGP_SPLITS_INVARIANT, 256);
   forward_case(4000, 1024, 50257, BILOGP_BIAS_F32, BILOGP_SPLITS_INVARIANT, 256);
   forward_case(4000, 1024, 50257, BILOGP_BIAS_NONE, BILOGP_SPLITS_INVARIANT, 80);
   backward_case(1024, 1024, 20480, BILOGP_BIAS_BF16, true);

@@ -82,6 +82,9 @@ MUTATIONS = {
     # a second launch sized from 256-token row blocks (its last rows never run)
     "tail_launch_too_few_row_blocks": ("  q.R = (int32_t)((p.N + 127) / 128);",
                                        "  q.R = (int32_t)((p.N + 255) / 256);"),
+    # a bf16 bias read directly where V cuts its last 16-byte chunk
+    "direct_bf16_bias_chunk_cut": ("  if (bias_dtype == BILOGP_BIAS_BF16) return V % 8 == 0;",
+                                   "  if (bias_dtype == BILOGP_BIAS_BF16) return V % 4 == 0;"),
 }
 
 

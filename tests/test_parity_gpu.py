@@ -199,11 +199,13 @@ def test_zero_weight_closed_form(V):
     assert torch.equal(logp, -lse), "logp != -lse with all logits zero"
 
 
-@pytest.mark.parametrize("V", [257, 259, 2 * 256 + 3, 16384 + 5])
+@pytest.mark.parametrize("V", [257, 259, 2 * 256 + 3, 2 * 256 + 8, 16384 + 4, 16384 + 5])
 @pytest.mark.parametrize("bias_dtype", [torch.bfloat16, torch.float32])
 def test_bias_on_ragged_vocab_tail(V, bias_dtype):
     """W = 0 and a unit-scale bias: every bias entry moves lse, and a target
-    in the last (partial) tile reads its own bias; checked against the oracle."""
+    in the last (partial) tile reads its own bias; checked against the oracle.
+    V = 520 (both dtypes) and 16388 (fp32) are read directly by the
+    projection, the rest through the zero-padded fp32 copy."""
     N, H = 40, 64
     g = torch.Generator().manual_seed(V)
     h = torch.randn(N, H, generator=g).to(torch.bfloat16)
@@ -216,6 +218,41 @@ def test_bias_on_ragged_vocab_tail(V, bias_dtype):
     torch.cuda.synchronize()
     ref_lp, ref_ls = oracle.linear_logp(h, w, t, b)
     assert_parity(logp, lse, ref_lp, ref_ls, tol=1e-4, what=f"bias tail V={V}")
+
+
+@pytest.mark.parametrize("bias_dtype", [torch.bfloat16, torch.float32])
+def test_bias_read_directly_or_through_the_copy_gives_the_same_bits(bias_dtype):
+    """A 16-byte-aligned bias with V a whole number of 16-byte chunks is read
+    by the projection directly; the same values one element past that
+    alignment go through the zero-padded fp32 copy.  The forward's outputs and
+    the backward's gradients are the same bits either way, and the forward
+    matches the oracle."""
+    N, H, V = 300, 256, 4096 + 8
+    g = torch.Generator().manual_seed(77)
+    h = torch.randn(N, H, generator=g).to(torch.bfloat16).to(DEV)
+    w = (torch.randn(V, H, generator=g) * 0.05).to(torch.bfloat16).to(DEV)
+    b = torch.randn(V, generator=g).to(bias_dtype).to(DEV)
+    t = torch.randint(0, V, (N,), generator=g).to(DEV)
+    t[:8] = torch.arange(V - 8, V, device=DEV)
+    shifted = torch.empty(V + 8, dtype=bias_dtype, device=DEV)[1:V + 1]
+    shifted.copy_(b)
+    assert b.data_ptr() % 16 == 0 and shifted.data_ptr() % 16 != 0
+    say(f"bias direct vs copy {bias_dtype} N={N} H={H} V={V}")
+    lp_d, ls_d = run_ex(h, w, t, b)
+    lp_c, ls_c = run_ex(h, w, t, shifted)
+    torch.cuda.synchronize()
+    assert torch.equal(lp_d, lp_c) and torch.equal(ls_d, ls_c)
+    ref_lp, ref_ls = oracle.linear_logp(h.cpu(), w.cpu(), t.cpu(), b.cpu())
+    assert_parity(lp_d, ls_d, ref_lp, ref_ls, what=f"bias direct {bias_dtype}")
+    gl = torch.randn(N, generator=g).to(DEV)
+    gs = torch.randn(N, generator=g).to(DEV)
+    grads = []
+    for bias in (b, shifted):
+        gh, gw, gb = ila.backward(h, w, t, bias, ls_d, gl, gs, bias_grad=True)
+        torch.cuda.synchronize()
+        grads.append((gh, gw, gb))
+    for x, y in zip(*grads):
+        assert torch.equal(x, y)
 
 
 @pytest.mark.parametrize("name", ["medium", "sweep"])
