@@ -578,6 +578,13 @@ def test_launch_plan_follows_the_compute_units_only_in_scheduling():
     assert ila.bilogp_launch_plan(8, 0, 1000, inv, 256) is None
     assert ila.bilogp_launch_plan(8, 64, 1000, inv, 0) is None
     assert ila.bilogp_launch_plan(8, 64, 1000, 7, 256) is None
+    for bad in ((0, 64, 1000, inv, 256), (8, 64, 0, inv, 256), (8, 0, 1000, inv, 256),
+                (8, 64, 1000, inv, 0), (8, 64, 1000, 7, 256), (8, 64, 1000, inv, 65537)):
+        assert ila.bilogp_launch_schedule(*bad) is None, bad
+    # the sweep shape on 256 units: 12 whole rounds of single splits, 6 splits left over
+    assert ila.bilogp_launch_schedule(4096, 4096, 151936, inv, 256) == (144, 192)
+    # the headline shape keeps one launch
+    assert ila.bilogp_launch_schedule(4096, 4096, 128256, inv, 256) == (251, 251)
     # the throughput mode's split count follows the same count
     assert ila.bilogp_launch_plan(8, 4096, 128256, tp, 256) is not None
 
