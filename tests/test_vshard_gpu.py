@@ -27,6 +27,9 @@ CASES = [  # N, H, V, bias, seed, cut points (split indices)
     (257, 264, 70000, "bf16", 2, [1, 27, 54, 100]),   # 137 splits of 2 tiles, last tile partial
     (1, 4096, 16385, "f32", 3, [16, 32]),        # 65 splits, last split one column
     (4096, 4096, 128256, None, 4, [32, 64, 96, 128, 160, 192, 224]),   # 8-way share of the headline
+    # on 256 compute units the full forward and both ranges end with a second,
+    # 128-token launch (16 x 198, 16 x 100 and 16 x 98 splits); bf16 bias read in place
+    (4096, 1024, 151936, "bf16", 5, [100]),
 ]
 
 
