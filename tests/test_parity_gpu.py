@@ -175,6 +175,19 @@ def test_peaky_sampled():
                                      g.choice(other, 254, replace=False), [0, wl.N - 1]]))
     ref_lp, ref_ls = oracle_rows(inp, rows=rows)
     assert_parity(logp, lse, ref_lp, ref_ls, rows=rows, what="peaky")
+    # On 256 compute units the full batch runs 49 whole rounds of 256-token
+    # tiles and its last 2 splits as 128-token pieces in a second launch; row
+    # chunks of 4000 and 1000 rows run other schedules.  Same bits.
+    h, t = flat(inp)
+    for chunk in (4000, 1000):
+        say(f"peaky row chunks of {chunk}")
+        lps, lss = [], []
+        for c0 in range(0, wl.N, chunk):
+            a, b = run_ex(h[c0:c0 + chunk], inp["weight"], t[c0:c0 + chunk], inp["bias"])
+            lps.append(a)
+            lss.append(b)
+        torch.cuda.synchronize()
+        assert torch.equal(torch.cat(lps), logp) and torch.equal(torch.cat(lss), lse), chunk
 
 
 @pytest.mark.parametrize("V", [1000, 32000, 128256, 152064])
