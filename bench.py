@@ -156,6 +156,22 @@ def time_forward(h, t, w, b, steps, warmup, stream):
     return proj, merge, step, ok
 
 
+def launch_plan(N, H, V):
+    """The projection launch the library makes on this device: row-block height,
+    splits per workgroup of the longest runs, workgroups over all launches, and
+    the split schedule (where single splits begin, where the 128-token second
+    launch begins; both = S when there is none)."""
+    import torch
+    import invariant_linear_log_amd as ila
+    cu = ila.device_cu_count(torch.device("cuda:0"))
+    inv = ila.BILOGP_SPLITS_INVARIANT
+    rows, spg, wgs = ila.bilogp_launch_plan(N, H, V, inv, cu)
+    sa, st = ila.bilogp_launch_schedule(N, H, V, inv, cu)
+    return {"rows_per_block": rows, "splits_per_workgroup": spg, "workgroups": wgs,
+            "split_a": sa, "split_t": st, "splits": ila.bilogp_num_vocab_splits(V),
+            "compute_units": cu}
+
+
 def config_legs(steps=10, warmup=3, names=("medium", "sweep", "peaky")):
     """The other single-GPU configurations, each timed like the headline (full
     forward step on resident inputs).  medium: N=512, H=1024, V=32000, fp32 bias;
@@ -184,7 +200,8 @@ def config_legs(steps=10, warmup=3, names=("medium", "sweep", "peaky")):
                      "merge_ms": sorted(merge)[len(merge) // 2],
                      "tokens_per_s": wl.N / sm * 1e3, "tflops": flops / sm / 1e9,
                      "proj_lse_tflops": flops / pm / 1e9,
-                     "frac": flops / pm / 1e9 / PEAK_BF16_TFLOPS, "outputs_sane": ok}
+                     "frac": flops / pm / 1e9 / PEAK_BF16_TFLOPS, "outputs_sane": ok,
+                     "launch": launch_plan(wl.N, wl.H, wl.V)}
         del inp, h, t, w, b
         torch.cuda.empty_cache()
     return out
@@ -629,6 +646,7 @@ def main():
                       "step_median": step_ms[K // 2], "step_min": step_ms[0]},
         "device": device_info(dev),
         "outputs_sane": ok,
+        "launch": launch_plan(N, H, V),
         "roofline": {"bound": "mfma", "kernel": "proj_lse_kernel",
                      "achieved": tflops_proj, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops_proj / PEAK_BF16_TFLOPS,
