@@ -557,7 +557,11 @@ __device__ __forceinline__ void proj_fwd_body(const ProjParams& p) {
       }
       load_bias(0);
     }
-    wait_vmcnt<0>();
+    // Stage 0 has landed once only the loads issued after it (the next
+    // stage's W slice, with three buffers also the hidden slice and W slice
+    // after it, and wave 0's bias) are outstanding: the counter completes in
+    // order.  Those are waited for at stage 0's own barrier.
+    if constexpr (kLoader) wait_vmcnt<kSlots == 2 ? kLoadsW : 2 * kLoadsW + kLoadsH>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     init_acc();
 #pragma unroll
